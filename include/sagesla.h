@@ -1,0 +1,135 @@
+/*
+ * sagesla.h — C ABI of the SageSLA forward on MI355X (gfx950).
+ *
+ * SageSLA is sparse-linear attention (SLA) whose exact branch uses
+ * SageAttention-style INT8 QK^T.  Pages: "揭秘TurboDiffusion：如何让视频生成实现百倍加速？"
+ * (sections "支柱一：低比特注意力加速 – SageAttention", "支柱二：稀疏线性注意力 – SLA":
+ * INT8 attention with outlier smoothing; exact attention on the important
+ * block interactions, ~90% sparse, plus a light linear-attention component;
+ * the two stack) and "TurboDiffusion深度解析…" (sections 2.1, 2.2: top-k
+ * sparse selection with sla_topk; linear complexity through a kernel-function
+ * approximation).
+ *
+ * Operator, per head (b,h) of Q, K, V in [B,H,N,d] bf16, blocks of 64 rows:
+ *   1. block means of Q and K (float32, rows summed in order);
+ *   2. mu = mean of K over the N tokens;
+ *   3. block scores s_ij = qbar_i . (kbar_j - mu) (float32 FMA chain);
+ *   4. per query block i keep the kb = clamp(floor(topk*T + 1e-6), 1, T)
+ *      highest-scoring key blocks (kb = 0 when topk = 0), ties to the lower j;
+ *   5. Q -> INT8, one scale amax/127 per 64-row block, round-half-even;
+ *   6. K' = K - mu -> INT8 likewise;
+ *   7. exact branch: softmax over the kept key blocks of the logits
+ *      (q8 . k8) * dq_i * dk_j * sm_scale, times V (bf16);
+ *   8. linear branch over the other ("marginal") key blocks:
+ *      phi(Q) H_i / (phi(Q) . z_i), H_i = sum of phi(K_s)^T V_s, z_i = sum of
+ *      phi(K_s), phi = softmax over the d channels;
+ *   9. out = O_sparse + O_linear W^T (W [d_out][d_in] bf16, no bias) when
+ *      use_linear, else O_sparse; out is bf16 [B,H,N,d].
+ * Steps 1-6 and the int32 products of 7 are reproduced bit for bit by the CPU
+ * oracle; the rest matches it within max-abs 2e-2 and relative-L2 1e-2.
+ *
+ * Conventions
+ *  - All device pointers are device memory of the current HIP device; all
+ *    tensors are contiguous, 16-byte aligned.  The workspace is owned by the
+ *    caller, at least sla_plan_info()'s workspace_bytes and 256-byte aligned;
+ *    one workspace may not serve two calls at once.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work: no device allocation, no host synchronisation.
+ *  - sla_quantize must run before sla_attention_fwd on the same workspace
+ *    and stream with the same q and k.
+ *  - Arguments are checked on the host before anything is launched; a launch
+ *    failure is reported as SLA_EHIP; device faults surface at the caller's
+ *    next synchronisation.
+ *  - Inputs must be finite.
+ */
+#ifndef SAGESLA_H
+#define SAGESLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA_OK = 0,
+  SLA_EINVAL = 1,        /* bad argument: null pointer, size, misalignment, topk */
+  SLA_EUNSUPPORTED = 2,  /* valid but not built: d not in {64,128}, block != 64, N too large */
+  SLA_EWORKSPACE = 3,    /* workspace smaller than sla_plan_info() says */
+  SLA_EHIP = 4,          /* a HIP launch failed */
+  SLA_ENOMEM = 5         /* host allocation of the plan failed */
+} sla_status;
+
+typedef struct {
+  int32_t B, H, N, d;  /* batch, heads, tokens (>= 1), head dim (64 or 128) */
+  int32_t block;       /* block size; must be 64 */
+  float topk;          /* kept fraction of key blocks, in [0, 1] (sla_topk) */
+  int32_t use_linear;  /* 1: add the projected linear branch; 0: sparse branch only */
+  float sm_scale;      /* softmax scale; 0 selects float32(1/sqrt(d)) */
+  int32_t qk_int8;     /* 1: INT8 QK^T (SageSLA); 0: bf16 QK^T (plain SLA) */
+} sla_config;
+
+typedef struct sla_plan_s *sla_plan_t;
+
+/* Validate cfg and build a plan (host only, no HIP call).  *out is set on
+ * SLA_OK.  The plan is immutable and may be shared by threads. */
+sla_status sla_plan(const sla_config *cfg, sla_plan_t *out);
+
+/* Free a plan (NULL is accepted). */
+sla_status sla_plan_destroy(sla_plan_t plan);
+
+/* T = number of 64-row blocks, kb = kept key blocks per query block,
+ * workspace_bytes = workspace size needed.  Any output pointer may be NULL. */
+sla_status sla_plan_info(sla_plan_t plan, int32_t *T, int32_t *kb, size_t *workspace_bytes);
+
+/* Selection and quantisation (steps 1-6): block pooling, K mean, block
+ * scores, top-k mask and kept lists, INT8 Q and K' with their scales, all into
+ * the workspace.  q, k: bf16 [B,H,N,d]. */
+sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* Attention (steps 7-9): V re-layout and per-key-block linear states,
+ * marginal-block states per query block, block-sparse INT8/bf16 flash
+ * attention with the linear branch and projection fused in its epilogue.
+ * w_proj: bf16 [d][d] ([d_out][d_in]); may be NULL when use_linear is 0.
+ * out: bf16 [B,H,N,d]; padding rows are never written. */
+sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
+                             const void *w_proj, void *out, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Static text for a status code. */
+const char *sla_status_string(sla_status s);
+
+/* Workspace regions, for tests and debugging (layouts in the comments). */
+enum {
+  SLA_WS_QBAR = 0, /* float [B*H][T][d]  block means of Q                         */
+  SLA_WS_KSUM = 1, /* float [B*H][T][d]  block sums of K                          */
+  SLA_WS_KBAR = 2, /* float [B*H][T][d]  block means of K                         */
+  SLA_WS_MU = 3,   /* float [B*H][d]     K channel mean                           */
+  SLA_WS_MASK = 4, /* uint64 [B*H][T][ceil(T/64)]  bit j%64 of word j/64 = kept   */
+  SLA_WS_KEPT = 5, /* int32 [B*H][T][kb] kept key blocks, ascending               */
+  SLA_WS_Q8 = 6,   /* int8 [B*H][T][64*d] per block, MFMA-fragment order:
+                      byte (((r/16)*(d/64) + c/64)*64 + r%16 + 16*((c%64)/16))*16 + c%16
+                      holds row r, channel c                                      */
+  SLA_WS_K8 = 7,   /* int8, same layout as Q8, of K - mu                          */
+  SLA_WS_DQ = 8,   /* float [B*H][T] Q block scales                               */
+  SLA_WS_DK = 9,   /* float [B*H][T] K' block scales                              */
+  SLA_WS_COUNT = 10
+};
+
+/* Device pointer and size of one workspace region. */
+sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr, size_t *bytes);
+
+/* The int32 QK^T block products the attention kernel computes, for n pairs
+ * given as int32 (bh, i, j) triples in device memory; dev_out receives n
+ * tiles of int32 [64 query rows][64 key rows].  Uses the same device code as
+ * the attention kernel.  Needs sla_quantize first and qk_int8 = 1. */
+sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *dev_pairs, int32_t n,
+                              int32_t *dev_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGESLA_H */

@@ -1,0 +1,202 @@
+// Block pooling, K channel mean and INT8 quantisation of Q and K - mu.
+//
+// Pages: "揭秘TurboDiffusion…" section "支柱一：低比特注意力加速 – SageAttention"
+// (attention in INT8 with outlier smoothing) and section "支柱二：稀疏线性注意力 – SLA"
+// (block selection from pooled blocks); "TurboDiffusion跨模态…" section
+// "SageAttention2++" (outlier smoothing).  The float32 operation order below is
+// part of the operator's definition (block means feed an integer decision, the
+// top-k mask): sums run over the rows of a block in order, the K mean over the
+// blocks in order, divisions are done in float64 and rounded once.
+//
+// Memory bound: each kernel streams its input once (Q, K: 2 x 2 bytes per
+// element read by the pooling kernel, K once more by the K quantiser) and
+// writes one byte per element.  Codes are staged in LDS so the global stores
+// are whole 16-byte lanes of a 1 KiB fragment.
+#include "sla_internal.h"
+
+namespace sla {
+
+// One wave per (head, block).  Lanes 0..D/4-1 own four channels of Q for all
+// 64 rows, lanes 32..32+D/4-1 the same channels of K; each lane adds its rows
+// in order (float32).  Q's values stay in registers for the quantisation.
+template <int D>
+__global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict__ Q,
+                                                      const uint16_t *__restrict__ K, int N, int T,
+                                                      int nblk, float *__restrict__ qbar,
+                                                      float *__restrict__ ksum,
+                                                      float *__restrict__ kbar,
+                                                      int8_t *__restrict__ q8,
+                                                      float *__restrict__ dq) {
+  constexpr int LPT = D / 4;  // lanes per tensor
+  constexpr int KC = D / 64;
+  __shared__ __attribute__((aligned(16))) int8_t stage[4][64 * D];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + w;
+  const bool live = blk < nblk;
+  const int bh = live ? blk / T : 0, t = live ? blk - (blk / T) * T : 0;
+  const int n = min(BLK, N - t * BLK);
+  const int half = l >> 5, cl = l & 31;
+  const bool act = live && cl < LPT;
+  const uint16_t *X = half ? K : Q;
+  const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + 4 * cl;
+
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, amax = 0.f;
+  uint2 vals[BLK];
+#pragma unroll
+  for (int r = 0; r < BLK; ++r) {
+    uint2 v = make_uint2(0u, 0u);
+    if (act && r < n) v = *(const uint2 *)(X + base + (size_t)r * D);
+    vals[r] = v;
+    if (act && r < n) {
+      float a = bf2f(v.x & 0xFFFF), b = bf2f(v.x >> 16), c = bf2f(v.y & 0xFFFF), d = bf2f(v.y >> 16);
+      s0 = s0 + a;
+      s1 = s1 + b;
+      s2 = s2 + c;
+      s3 = s3 + d;
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
+    }
+  }
+  if (act) {
+    const size_t o = ((size_t)blk) * D + 4 * cl;
+    const double dn = (double)n;
+    float4 mean = make_float4((float)((double)s0 / dn), (float)((double)s1 / dn),
+                              (float)((double)s2 / dn), (float)((double)s3 / dn));
+    if (half == 0) {
+      *(float4 *)(qbar + o) = mean;
+    } else {
+      *(float4 *)(ksum + o) = make_float4(s0, s1, s2, s3);
+      *(float4 *)(kbar + o) = mean;
+    }
+  }
+  // block amax of Q over lanes 0..31 (max is exact in any order)
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = __shfl(amax, 0, 64);
+  const float delta = (float)((double)amax / 127.0);
+  const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+  if (live && l == 0) dq[blk] = delta;
+
+  if (half == 0 && cl < LPT) {
+#pragma unroll
+    for (int r = 0; r < BLK; ++r) {
+      uint2 v = vals[r];
+      float x[4] = {bf2f(v.x & 0xFFFF), bf2f(v.x >> 16), bf2f(v.y & 0xFFFF), bf2f(v.y >> 16)};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = __builtin_rintf(x[e] * inv);
+        y = fminf(fmaxf(y, -127.f), 127.f);
+        packed |= ((uint32_t)(uint8_t)(int8_t)(int)y) << (8 * e);
+      }
+      if (r >= n) packed = 0;
+      *(uint32_t *)(&stage[w][i8_off(r, 4 * cl, KC)]) = packed;
+    }
+  }
+  __syncthreads();
+  if (live) {
+    const uint4 *src = (const uint4 *)stage[w];
+    uint4 *dst = (uint4 *)(q8 + (size_t)blk * BLK * D);
+#pragma unroll
+    for (int it = 0; it < (BLK * D) / (16 * 64); ++it) dst[it * 64 + l] = src[it * 64 + l];
+  }
+}
+
+// mu[bh][c] = float32((sum over blocks t in order of ksum[bh][t][c]) / N).
+__global__ void k_kmean(const float *__restrict__ ksum, int N, int T, int D, float *__restrict__ mu) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const float *p = ksum + (size_t)bh * T * D + c;
+  float s = 0.f;
+  for (int t = 0; t < T; ++t) s = s + p[(size_t)t * D];
+  mu[(size_t)bh * D + c] = (float)((double)s / (double)N);
+}
+
+// One wave per (head, block): k' = float32(K - mu[c]); amax over the valid rows;
+// codes = rint(k' * float32(127/amax)) clamped to [-127, 127].
+template <int D>
+__global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
+                                                 const float *__restrict__ mu, int N, int T,
+                                                 int nblk, int8_t *__restrict__ k8,
+                                                 float *__restrict__ dk) {
+  constexpr int LPR = D / 4;       // lanes per row
+  constexpr int RPI = 64 / LPR;    // rows per step
+  constexpr int STEPS = BLK / RPI;
+  constexpr int KC = D / 64;
+  __shared__ __attribute__((aligned(16))) int8_t stage[4][64 * D];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + w;
+  const bool live = blk < nblk;
+  const int bh = live ? blk / T : 0, t = live ? blk - (blk / T) * T : 0;
+  const int n = min(BLK, N - t * BLK);
+  const int c0 = 4 * (l % LPR), r0 = l / LPR;
+  const float4 m4 = *(const float4 *)(mu + (size_t)bh * D + c0);
+  const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + c0;
+
+  float xs[STEPS][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int r = s * RPI + r0;
+    uint2 v = make_uint2(0u, 0u);
+    const bool ok = live && r < n;
+    if (ok) v = *(const uint2 *)(K + base + (size_t)r * D);
+    xs[s][0] = bf2f(v.x & 0xFFFF) - m4.x;
+    xs[s][1] = bf2f(v.x >> 16) - m4.y;
+    xs[s][2] = bf2f(v.y & 0xFFFF) - m4.z;
+    xs[s][3] = bf2f(v.y >> 16) - m4.w;
+    if (ok)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xs[s][0]), fabsf(xs[s][1])),
+                               fmaxf(fabsf(xs[s][2]), fabsf(xs[s][3]))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float delta = (float)((double)amax / 127.0);
+  const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+  if (live && l == 0) dk[blk] = delta;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int r = s * RPI + r0;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y = __builtin_rintf(xs[s][e] * inv);
+      y = fminf(fmaxf(y, -127.f), 127.f);
+      packed |= ((uint32_t)(uint8_t)(int8_t)(int)y) << (8 * e);
+    }
+    if (r >= n) packed = 0;
+    *(uint32_t *)(&stage[w][i8_off(r, c0, KC)]) = packed;
+  }
+  __syncthreads();
+  if (live) {
+    const uint4 *src = (const uint4 *)stage[w];
+    uint4 *dst = (uint4 *)(k8 + (size_t)blk * BLK * D);
+#pragma unroll
+    for (int it = 0; it < (BLK * D) / (16 * 64); ++it) dst[it * 64 + l] = src[it * 64 + l];
+  }
+}
+
+void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, const WsPtrs &ws,
+                         hipStream_t st) {
+  const int nblk = p.BH * p.T;
+  dim3 grid((nblk + 3) / 4), block(256);
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_pool_quant_q<128>, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar,
+                       ws.ksum, ws.kbar, ws.q8, ws.dq);
+  else
+    hipLaunchKernelGGL(k_pool_quant_q<64>, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar,
+                       ws.ksum, ws.kbar, ws.q8, ws.dq);
+}
+
+void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st) {
+  hipLaunchKernelGGL(k_kmean, dim3(p.BH), dim3(p.d), 0, st, ws.ksum, p.N, p.T, p.d, ws.mu);
+}
+
+void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st) {
+  const int nblk = p.BH * p.T;
+  dim3 grid((nblk + 3) / 4), block(256);
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_quant_k<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk);
+  else
+    hipLaunchKernelGGL(k_quant_k<64>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk);
+}
+
+}  // namespace sla

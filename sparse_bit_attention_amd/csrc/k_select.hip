@@ -1,0 +1,147 @@
+// Block scores and per-row top-k selection.
+//
+// Pages: "TurboDiffusion深度解析…" section 2.1 (Top-K sparse selection, sla_topk)
+// and section 2.2 (sla_topk 0.05 / 0.1 / 0.15); "揭秘TurboDiffusion…" section
+// "支柱二：稀疏线性注意力 – SLA" (only the most important block interactions get
+// exact attention, ~90% sparsity).
+//
+// s_ij = qbar_i . (kbar_j - mu) is one float32 FMA chain over the channels in
+// order from +0, so the scores, and hence the mask, are reproducible bit for
+// bit.  Each row keeps the kb largest scores, ties to the lower block index.
+//
+// Work: T*T*d FMAs per head (plain fp32 ALU) and a 32-step bitwise threshold
+// search per row.  One workgroup holds R query-block means and R score rows in
+// LDS; each thread keeps one key block's (kbar - mu) in registers and walks the
+// R rows, reading qbar as LDS broadcasts.
+#include "sla_internal.h"
+
+namespace sla {
+
+// Monotone map of a finite float32 to uint32 (larger float -> larger key);
+// +0 and -0 map to the same key.  Never 0 for a finite float.
+__device__ __forceinline__ uint32_t score_key(float v) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave selects row `srow` (T scores in LDS): mask words (W64 of them) and
+// the ascending kept list (kb entries).
+__device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, int32_t *krow,
+                           int lane) {
+  const int E = (T + 63) >> 6;
+  if (kb <= 0) {
+    for (int e = lane; e < E; e += 64) mrow[e] = 0ull;
+    return;
+  }
+  // th = the kb-th largest key: the largest th with #{key >= th} >= kb,
+  // built one bit at a time from the top.
+  uint32_t th = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int cnt = 0;
+    for (int e = 0; e < E; ++e) {
+      const int j = e * 64 + lane;
+      const bool ge = j < T && score_key(srow[j]) >= cand;
+      cnt += __popcll(__ballot(ge));
+    }
+    if (cnt >= kb) th = cand;
+  }
+  int gt = 0;
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 64 + lane;
+    gt += __popcll(__ballot(j < T && score_key(srow[j]) > th));
+  }
+  int need = kb - gt;  // ties at th still to take, lowest index first
+  int pos = 0;
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 64 + lane;
+    const uint32_t key = j < T ? score_key(srow[j]) : 0u;
+    const uint64_t bgt = __ballot(j < T && key > th);
+    uint64_t beq = __ballot(j < T && key == th);
+    uint64_t take = 0ull;
+    if (need > 0) {
+      if (__popcll(beq) <= need) {
+        take = beq;
+      } else {
+        for (int q = 0; q < need; ++q) {
+          take |= beq & (~beq + 1ull);
+          beq &= beq - 1ull;
+        }
+      }
+      need -= __popcll(take);
+    }
+    const uint64_t sel = bgt | take;
+    if (lane == 0) mrow[e] = sel;
+    if ((sel >> lane) & 1ull) krow[pos + __popcll(sel & ((1ull << lane) - 1ull))] = j;
+    pos += __popcll(sel);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ qbar,
+                                                     const float *__restrict__ kbar,
+                                                     const float *__restrict__ mu, int T, int R,
+                                                     int kb, int W64,
+                                                     uint64_t *__restrict__ mask,
+                                                     int32_t *__restrict__ kept) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float *sq = smem;          // [R][D]
+  float *ss = smem + R * D;  // [R][T]
+  const int groups = (T + R - 1) / R;
+  const int bh = blockIdx.x / groups;
+  const int i0 = (blockIdx.x - bh * groups) * R;
+  const int nr = min(R, T - i0);
+  const int tid = threadIdx.x;
+  for (int x = tid; x < nr * D; x += 256) sq[x] = qbar[((size_t)bh * T + i0) * D + x];
+  __syncthreads();
+  for (int jb = 0; jb < T; jb += 256) {
+    const int j = jb + tid;
+    if (j < T) {
+      float kt[D];
+      const float4 *kp = (const float4 *)(kbar + ((size_t)bh * T + j) * D);
+      const float4 *mp = (const float4 *)(mu + (size_t)bh * D);
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) {
+        float4 a = kp[c], m = mp[c];
+        kt[4 * c + 0] = a.x - m.x;
+        kt[4 * c + 1] = a.y - m.y;
+        kt[4 * c + 2] = a.z - m.z;
+        kt[4 * c + 3] = a.w - m.w;
+      }
+      for (int r = 0; r < nr; ++r) {
+        const float4 *qr = (const float4 *)(sq + r * D);
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+          const float4 q = qr[c];
+          acc = __builtin_fmaf(q.x, kt[4 * c + 0], acc);
+          acc = __builtin_fmaf(q.y, kt[4 * c + 1], acc);
+          acc = __builtin_fmaf(q.z, kt[4 * c + 2], acc);
+          acc = __builtin_fmaf(q.w, kt[4 * c + 3], acc);
+        }
+        ss[r * T + j] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  const int w = tid >> 6, lane = tid & 63;
+  for (int r = w; r < nr; r += 4) {
+    const size_t row = (size_t)bh * T + i0 + r;
+    select_row(ss + r * T, T, kb, mask + row * W64, kept + row * (size_t)(kb > 0 ? kb : 1), lane);
+  }
+}
+
+void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st) {
+  const int R = p.rows_sel;
+  const int groups = (p.T + R - 1) / R;
+  const size_t lds = sizeof(float) * (size_t)R * (p.d + p.T);
+  dim3 grid(p.BH * groups), block(256);
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_scores_topk<128>, grid, block, lds, st, ws.qbar, ws.kbar, ws.mu, p.T, R,
+                       p.kb, p.W64, ws.mask, ws.kept);
+  else
+    hipLaunchKernelGGL(k_scores_topk<64>, grid, block, lds, st, ws.qbar, ws.kbar, ws.mu, p.T, R,
+                       p.kb, p.W64, ws.mask, ws.kept);
+}
+
+}  // namespace sla

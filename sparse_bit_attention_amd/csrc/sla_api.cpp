@@ -1,0 +1,226 @@
+// C ABI of libsagesla: plan validation, workspace map and launch sequencing.
+// All checks run on the host before anything is enqueued.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "sla_internal.h"
+
+struct sla_plan_s {
+  sla::Plan p;
+};
+
+namespace sla {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsPtrs ws_ptrs(const Plan &p, void *ws) {
+  char *b = (char *)ws;
+  WsPtrs w;
+  w.qbar = (float *)(b + p.off[R_QBAR]);
+  w.ksum = (float *)(b + p.off[R_KSUM]);
+  w.kbar = (float *)(b + p.off[R_KBAR]);
+  w.mu = (float *)(b + p.off[R_MU]);
+  w.mask = (uint64_t *)(b + p.off[R_MASK]);
+  w.kept = (int32_t *)(b + p.off[R_KEPT]);
+  w.q8 = (int8_t *)(b + p.off[R_Q8]);
+  w.k8 = (int8_t *)(b + p.off[R_K8]);
+  w.dq = (float *)(b + p.off[R_DQ]);
+  w.dk = (float *)(b + p.off[R_DK]);
+  w.vt = (uint16_t *)(b + p.off[R_VT]);
+  w.qb = (uint16_t *)(b + p.off[R_QB]);
+  w.kbf = (uint16_t *)(b + p.off[R_KB]);
+  w.wsw = (uint16_t *)(b + p.off[R_WSW]);
+  w.hb = (uint16_t *)(b + p.off[R_HB]);
+  w.hi = (uint16_t *)(b + p.off[R_HI]);
+  return w;
+}
+
+// Rows of query blocks per selection workgroup: R*(d + T) floats must fit in
+// 64 KiB of LDS; a multiple of 4 (one row per wave) when possible.
+static int selection_rows(int d, int T) {
+  long r = (64L * 1024 / 4) / (long)(d + T);
+  if (r > 16) r = 16;
+  if (r >= 4) r &= ~3L;
+  return (int)r;
+}
+
+}  // namespace sla
+
+using namespace sla;
+
+extern "C" {
+
+const char *sla_status_string(sla_status s) {
+  switch (s) {
+    case SLA_OK: return "ok";
+    case SLA_EINVAL: return "invalid argument";
+    case SLA_EUNSUPPORTED: return "unsupported configuration";
+    case SLA_EWORKSPACE: return "workspace too small";
+    case SLA_EHIP: return "HIP launch failed";
+    case SLA_ENOMEM: return "host allocation failed";
+  }
+  return "unknown status";
+}
+
+sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
+  if (!cfg || !out) return SLA_EINVAL;
+  const sla_config c = *cfg;
+  if (c.B < 1 || c.H < 1 || c.N < 1) return SLA_EINVAL;
+  if (!(c.topk >= 0.0f && c.topk <= 1.0f)) return SLA_EINVAL;
+  if (c.use_linear != 0 && c.use_linear != 1) return SLA_EINVAL;
+  if (c.qk_int8 != 0 && c.qk_int8 != 1) return SLA_EINVAL;
+  if (!(c.sm_scale >= 0.0f) || isinf(c.sm_scale)) return SLA_EINVAL;
+  if (c.block != BLK) return SLA_EUNSUPPORTED;
+  if (c.d != 64 && c.d != 128) return SLA_EUNSUPPORTED;
+  if (c.qk_int8 != 1) return SLA_EUNSUPPORTED;
+  const long long T = ((long long)c.N + BLK - 1) / BLK;
+  const long long BH = (long long)c.B * c.H;
+  if (sla::selection_rows(c.d, (int)(T > (1 << 30) ? (1 << 30) : T)) < 1) return SLA_EUNSUPPORTED;
+  if (BH * T >= (1LL << 31) / BLK) return SLA_EUNSUPPORTED;
+
+  sla_plan_s *h = new (std::nothrow) sla_plan_s;
+  if (!h) return SLA_ENOMEM;
+  Plan &p = h->p;
+  memset(&p, 0, sizeof p);
+  p.cfg = c;
+  p.B = c.B;
+  p.H = c.H;
+  p.N = c.N;
+  p.d = c.d;
+  p.BH = (int)BH;
+  p.T = (int)T;
+  {
+    // kb = 0 for topk = 0, else clamp(floor(topk*T + 1e-6), 1, T), in float64
+    long kb = 0;
+    if ((double)c.topk > 0.0) {
+      kb = (long)floor((double)c.topk * (double)p.T + 1e-6);
+      if (kb < 1) kb = 1;
+      if (kb > p.T) kb = p.T;
+    }
+    p.kb = (int)kb;
+  }
+  p.W64 = (p.T + 63) / 64;
+  p.F = ((c.d * c.d + c.d) + 127) / 128 * 128;
+  p.rows_sel = selection_rows(c.d, p.T);
+  p.lin_on = (c.use_linear == 1 && p.kb < p.T) ? 1 : 0;
+  p.qk_int8 = c.qk_int8;
+  p.sm_scale = c.sm_scale > 0.0f ? c.sm_scale : (float)(1.0 / sqrt((double)c.d));
+
+  const size_t bt = (size_t)p.BH * p.T;
+  const size_t blk_elems = bt * BLK * p.d;
+  p.size[R_QBAR] = bt * p.d * 4;
+  p.size[R_KSUM] = bt * p.d * 4;
+  p.size[R_KBAR] = bt * p.d * 4;
+  p.size[R_MU] = (size_t)p.BH * p.d * 4;
+  p.size[R_MASK] = bt * p.W64 * 8;
+  p.size[R_KEPT] = bt * (size_t)(p.kb > 0 ? p.kb : 1) * 4;
+  p.size[R_Q8] = blk_elems;
+  p.size[R_K8] = blk_elems;
+  p.size[R_DQ] = bt * 4;
+  p.size[R_DK] = bt * 4;
+  p.size[R_VT] = blk_elems * 2;
+  p.size[R_QB] = p.qk_int8 ? 0 : blk_elems * 2;
+  p.size[R_KB] = p.qk_int8 ? 0 : blk_elems * 2;
+  p.size[R_WSW] = p.lin_on ? (size_t)p.d * p.d * 2 : 0;
+  p.size[R_HB] = p.lin_on ? bt * p.F * 2 : 0;
+  p.size[R_HI] = p.lin_on ? bt * p.F * 2 : 0;
+  size_t o = 0;
+  for (int r = 0; r < R_COUNT; ++r) {
+    p.off[r] = o;
+    o += align256(p.size[r]);
+  }
+  p.total = o;
+  *out = h;
+  return SLA_OK;
+}
+
+sla_status sla_plan_destroy(sla_plan_t plan) {
+  delete plan;
+  return SLA_OK;
+}
+
+sla_status sla_plan_info(sla_plan_t plan, int32_t *T, int32_t *kb, size_t *workspace_bytes) {
+  if (!plan) return SLA_EINVAL;
+  if (T) *T = plan->p.T;
+  if (kb) *kb = plan->p.kb;
+  if (workspace_bytes) *workspace_bytes = plan->p.total;
+  return SLA_OK;
+}
+
+static bool aligned(const void *x, size_t a) { return ((uintptr_t)x % a) == 0; }
+
+static sla_status check_ws(const Plan &p, const void *ws, size_t ws_bytes) {
+  if (!ws) return SLA_EINVAL;
+  if (!aligned(ws, 256)) return SLA_EINVAL;
+  if (ws_bytes < p.total) return SLA_EWORKSPACE;
+  return SLA_OK;
+}
+
+static sla_status launched() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SLA_OK : SLA_EHIP;
+}
+
+sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws, size_t ws_bytes,
+                        void *stream) {
+  if (!plan || !q || !k) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (!aligned(q, 16) || !aligned(k, 16)) return SLA_EINVAL;
+  sla_status s = check_ws(p, ws, ws_bytes);
+  if (s != SLA_OK) return s;
+  (void)hipGetLastError();
+  hipStream_t st = (hipStream_t)stream;
+  WsPtrs w = ws_ptrs(p, ws);
+  launch_pool_quant_q(p, (const uint16_t *)q, (const uint16_t *)k, w, st);
+  launch_kmean(p, w, st);
+  launch_select(p, w, st);
+  launch_quant_k(p, (const uint16_t *)k, w, st);
+  return launched();
+}
+
+sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
+                             const void *w_proj, void *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  if (!plan || !q || !k || !v || !out) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (p.cfg.use_linear && !w_proj) return SLA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SLA_EINVAL;
+  if (w_proj && !aligned(w_proj, 16)) return SLA_EINVAL;
+  sla_status s = check_ws(p, ws, ws_bytes);
+  if (s != SLA_OK) return s;
+  (void)hipGetLastError();
+  hipStream_t st = (hipStream_t)stream;
+  WsPtrs w = ws_ptrs(p, ws);
+  launch_kv_prep(p, (const uint16_t *)k, (const uint16_t *)v, w, st);
+  if (p.lin_on) {
+    launch_w_swizzle(p, (const uint16_t *)w_proj, w, st);
+    launch_marginal(p, w, st);
+  }
+  launch_attn(p, (const uint16_t *)q, w, (uint16_t *)out, st);
+  return launched();
+}
+
+sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr, size_t *bytes) {
+  if (!plan || !dev_ptr || !bytes) return SLA_EINVAL;
+  if (which < 0 || which >= SLA_WS_COUNT) return SLA_EINVAL;
+  *dev_ptr = (char *)ws + plan->p.off[which];
+  *bytes = plan->p.size[which];
+  return SLA_OK;
+}
+
+sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *dev_pairs, int32_t n,
+                              int32_t *dev_out, void *stream) {
+  if (!plan || !ws || n < 0 || (n > 0 && (!dev_pairs || !dev_out))) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (!p.qk_int8) return SLA_EUNSUPPORTED;
+  if (!aligned(ws, 256)) return SLA_EINVAL;
+  (void)hipGetLastError();
+  WsPtrs w = ws_ptrs(p, (void *)ws);
+  launch_debug_qk(p, w, dev_pairs, n, dev_out, (hipStream_t)stream);
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal plan, workspace map and kernel launchers of libsagesla.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sagesla.h"
+#include "sla_device.h"
+
+namespace sla {
+
+// Workspace regions in order; the first SLA_WS_COUNT match the public enum.
+enum Region {
+  R_QBAR = SLA_WS_QBAR,
+  R_KSUM = SLA_WS_KSUM,
+  R_KBAR = SLA_WS_KBAR,
+  R_MU = SLA_WS_MU,
+  R_MASK = SLA_WS_MASK,
+  R_KEPT = SLA_WS_KEPT,
+  R_Q8 = SLA_WS_Q8,
+  R_K8 = SLA_WS_K8,
+  R_DQ = SLA_WS_DQ,
+  R_DK = SLA_WS_DK,
+  R_VT,   // bf16 V per key block in kmaj_off order              [BH][T][64*d]
+  R_QB,   // bf16 Q per query block, fragment order (bf16 QK^T)  [BH][T][64*d]
+  R_KB,   // bf16 K per key block, fragment order (bf16 QK^T)    [BH][T][64*d]
+  R_WSW,  // bf16 projection in wfrag_off order                  [d*d]
+  R_HB,   // bf16 per key block linear state (hstate_off order)  [BH][T][F]
+  R_HI,   // bf16 per query block marginal state (same order)    [BH][T][F]
+  R_COUNT
+};
+
+struct Plan {
+  sla_config cfg;
+  int B, H, N, d, BH, T, kb, W64;
+  int F;          // per-block linear-state length, d*d + d padded to 128
+  int rows_sel;   // query-block rows per selection workgroup
+  int lin_on;     // linear branch present (use_linear and kb < T)
+  int qk_int8;
+  float sm_scale;
+  size_t off[R_COUNT], size[R_COUNT], total;
+};
+
+struct WsPtrs {
+  float *qbar, *ksum, *kbar, *mu, *dq, *dk;
+  uint64_t *mask;
+  int32_t *kept;
+  int8_t *q8, *k8;
+  uint16_t *vt, *qb, *kbf, *wsw, *hb, *hi;
+};
+
+WsPtrs ws_ptrs(const Plan &p, void *ws);
+
+void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, const WsPtrs &ws,
+                         hipStream_t st);
+void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st);
+void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st);
+void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st);
+void launch_bf16_frags(const Plan &p, const uint16_t *q, const uint16_t *k, const WsPtrs &ws,
+                       hipStream_t st);
+void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const WsPtrs &ws,
+                    hipStream_t st);
+void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st);
+void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st);
+void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st);
+void launch_debug_qk(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n, int32_t *out,
+                     hipStream_t st);
+
+}  // namespace sla

@@ -1,0 +1,208 @@
+"""ctypes binding of libsagesla (argument marshalling only).
+
+Every step of the forward runs in the HIP kernels behind ``include/sagesla.h``;
+PyTorch only supplies device memory and the stream.  Importing this module
+raises if the library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsagesla.so")
+
+SLA_OK, SLA_EINVAL, SLA_EUNSUPPORTED, SLA_EWORKSPACE, SLA_EHIP, SLA_ENOMEM = range(6)
+WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "DK"]
+
+EXPORTS = ["sla_plan", "sla_plan_destroy", "sla_plan_info", "sla_quantize", "sla_attention_fwd",
+           "sla_status_string", "sla_ws_view", "sla_debug_qk_int32"]
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class sla_config(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_float),
+                ("use_linear", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("qk_int8", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_bit_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.sla_plan.argtypes = [ctypes.POINTER(sla_config), ctypes.POINTER(P)]
+        L.sla_plan.restype = ctypes.c_int
+        L.sla_plan_destroy.argtypes = [P]
+        L.sla_plan_destroy.restype = ctypes.c_int
+        L.sla_plan_info.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        L.sla_plan_info.restype = ctypes.c_int
+        L.sla_quantize.argtypes = [P, P, P, P, sz, P]
+        L.sla_quantize.restype = ctypes.c_int
+        L.sla_attention_fwd.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.sla_attention_fwd.restype = ctypes.c_int
+        L.sla_status_string.argtypes = [ctypes.c_int]
+        L.sla_status_string.restype = ctypes.c_char_p
+        L.sla_ws_view.argtypes = [P, P, i32, ctypes.POINTER(P), ctypes.POINTER(sz)]
+        L.sla_ws_view.restype = ctypes.c_int
+        L.sla_debug_qk_int32.argtypes = [P, P, P, i32, P, P]
+        L.sla_debug_qk_int32.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().sla_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SLA_OK:
+        raise SlaError(status, where)
+
+
+@dataclass
+class PlanInfo:
+    T: int
+    kb: int
+    workspace_bytes: int
+
+
+class Plan:
+    """Owns an ``sla_plan_t``."""
+
+    def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True, block=64):
+        self.cfg = sla_config(B, H, N, d, block, topk, int(use_linear), sm_scale, int(qk_int8))
+        h = ctypes.c_void_p()
+        _check(lib().sla_plan(ctypes.byref(self.cfg), ctypes.byref(h)), "sla_plan")
+        self.handle = h
+        T, kb, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+        _check(lib().sla_plan_info(h, ctypes.byref(T), ctypes.byref(kb), ctypes.byref(ws)),
+               "sla_plan_info")
+        self.info = PlanInfo(T.value, kb.value, ws.value)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.sla_plan_destroy(h)
+            self.handle = None
+
+    def ws_region(self, ws_ptr: int, which: str):
+        p, n = ctypes.c_void_p(), ctypes.c_size_t()
+        _check(lib().sla_ws_view(self.handle, ctypes.c_void_p(ws_ptr), WS_REGIONS.index(which),
+                                 ctypes.byref(p), ctypes.byref(n)), "sla_ws_view")
+        return (p.value or 0) - ws_ptr, n.value
+
+
+class SageSLA:
+    """SageSLA forward on [B, H, N, d] bf16 CUDA (HIP) tensors."""
+
+    def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True,
+                 device="cuda"):
+        import torch
+        self.plan = Plan(B, H, N, d, topk, use_linear, sm_scale, qk_int8)
+        self.shape = (B, H, N, d)
+        self.use_linear = bool(use_linear)
+        self.device = torch.device(device)
+        self.ws = torch.empty(max(self.plan.info.workspace_bytes, 256), dtype=torch.uint8,
+                              device=self.device)
+
+    # -- helpers ---------------------------------------------------------------
+    def _tensor(self, x, name, shape):
+        import torch
+        if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+        return ctypes.c_void_p(x.data_ptr())
+
+    @staticmethod
+    def _stream(stream):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return ctypes.c_void_p(s.cuda_stream)
+
+    # -- the two calls ---------------------------------------------------------
+    def quantize(self, q, k, stream=None):
+        _check(lib().sla_quantize(self.plan.handle, self._tensor(q, "q", self.shape),
+                                  self._tensor(k, "k", self.shape),
+                                  ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                  self._stream(stream)), "sla_quantize")
+
+    def attention(self, q, k, v, w=None, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
+        d = self.shape[3]
+        wp = self._tensor(w, "w", (d, d)) if w is not None else ctypes.c_void_p(0)
+        _check(lib().sla_attention_fwd(self.plan.handle, self._tensor(q, "q", self.shape),
+                                       self._tensor(k, "k", self.shape),
+                                       self._tensor(v, "v", self.shape), wp,
+                                       self._tensor(out, "out", self.shape),
+                                       ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                       self._stream(stream)), "sla_attention_fwd")
+        return out
+
+    def forward(self, q, k, v, w=None, out=None, stream=None):
+        self.quantize(q, k, stream)
+        return self.attention(q, k, v, w, out, stream)
+
+    __call__ = forward
+
+    # -- debug views -----------------------------------------------------------
+    def region(self, which: str):
+        """A torch view of one workspace region (see sagesla.h)."""
+        import torch
+        off, n = self.plan.ws_region(self.ws.data_ptr(), which)
+        raw = self.ws[off:off + n]
+        B, H, N, d = self.shape
+        T, kb = self.plan.info.T, self.plan.info.kb
+        BH = B * H
+        if which in ("QBAR", "KSUM", "KBAR"):
+            return raw.view(torch.float32).view(BH, T, d)
+        if which == "MU":
+            return raw.view(torch.float32).view(BH, d)
+        if which in ("DQ", "DK"):
+            return raw.view(torch.float32).view(BH, T)
+        if which == "MASK":
+            return raw.view(torch.int64).view(BH, T, (T + 63) // 64)
+        if which == "KEPT":
+            return raw.view(torch.int32).view(BH, T, max(kb, 1))[:, :, :kb]
+        if which in ("Q8", "K8"):
+            return raw.view(torch.int8).view(BH, T, 64 * d)
+        raise KeyError(which)
+
+    def debug_qk_int32(self, triples, stream=None):
+        """int32 QK^T tiles [n, 64, 64] for (bh, i, j) triples."""
+        import torch
+        t = torch.as_tensor(triples, dtype=torch.int32).reshape(-1, 3).contiguous().to(self.device)
+        n = t.shape[0]
+        out = torch.empty((n, 64, 64), dtype=torch.int32, device=self.device)
+        _check(lib().sla_debug_qk_int32(self.plan.handle, ctypes.c_void_p(self.ws.data_ptr()),
+                                        ctypes.c_void_p(t.data_ptr()), n,
+                                        ctypes.c_void_p(out.data_ptr()), self._stream(stream)),
+               "sla_debug_qk_int32")
+        return out
+
+
+def i8_unswizzle(tiles, d):
+    """Fragment-ordered INT8 blocks [..., 64*d] -> row-major [..., 64, d]
+    (pure index permutation, layout documented in sagesla.h)."""
+    import numpy as np
+    r = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    KC = d // 64
+    off = ((((r >> 4) * KC + (c >> 6)) * 64 + (r & 15) + 16 * ((c & 63) >> 4)) << 4) + (c & 15)
+    return np.asarray(tiles)[..., off]

@@ -1,0 +1,241 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: block means and sums, K mean, mask bits, kept lists, INT8 codes and
+scales, int32 QK^T tiles.  Outputs: max-abs <= 2e-2 and relative L2 <= 1e-2
+against the float64 oracle (the bar the operator is specified with); the
+measured values are printed and are far below it.
+
+Small cases compare every head and every query block.  The Wan-shaped
+workloads run at full size in the launch configuration the benchmark times
+and compare sampled heads (all masks and codes of those heads) and sampled
+query blocks (outputs), plus properties checked on every head.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_bit_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_bit_attention_amd import sla  # noqa: E402  (raises if the library is missing)
+
+MAX_ABS, REL_L2 = 2e-2, 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def host_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32(b):
+    return synth.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def run(wl: synth.Workload, inputs=None, sm_scale=0.0, out=None):
+    if inputs is None:
+        inputs = synth.all_inputs(wl)
+    q, k, v, w = inputs
+    Q, K, V, W = dev(q), dev(k), dev(v), dev(w)
+    m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear),
+                    sm_scale=sm_scale)
+    say(f"[gpu] forward {wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} topk={wl.topk} "
+        f"lin={wl.use_linear} kb={m.plan.info.kb}")
+    o = m(Q, K, V, W if wl.use_linear else None, out=out)
+    torch.cuda.synchronize()
+    return m, o, (Q, K, V, W), inputs
+
+
+def unpack_mask(words, T):
+    bits = np.unpackbits(np.ascontiguousarray(words).view(np.uint8).reshape(*words.shape, 8),
+                         axis=-1, bitorder="little")
+    return bits.reshape(words.shape[0], -1)[:, :T]
+
+
+def check_head_prep(m, wl, b, h, Qh, Kh):
+    bh = b * wl.H + h
+    prep = oracle.head_prep(Qh, Kh, float(np.float32(wl.topk)))
+    T, kb, d = m.plan.info.T, m.plan.info.kb, wl.d
+    g = {r: m.region(r)[bh].cpu().numpy() for r in ("QBAR", "KSUM", "KBAR", "MU", "DQ", "DK")}
+    assert np.array_equal(g["QBAR"].view(np.uint32), prep.qbar.view(np.uint32))
+    assert np.array_equal(g["KSUM"].view(np.uint32), prep.ksum.view(np.uint32))
+    assert np.array_equal(g["KBAR"].view(np.uint32), prep.kbar.view(np.uint32))
+    assert np.array_equal(g["MU"].view(np.uint32), prep.mu.view(np.uint32))
+    mask = unpack_mask(m.region("MASK")[bh].cpu().numpy(), T)
+    assert np.array_equal(mask, prep.mask), f"mask differs in {int((mask != prep.mask).sum())} places"
+    if kb:
+        assert np.array_equal(m.region("KEPT")[bh].cpu().numpy(), prep.kept)
+    q8 = sla.i8_unswizzle(m.region("Q8")[bh].cpu().numpy(), d).reshape(T * 64, d)
+    k8 = sla.i8_unswizzle(m.region("K8")[bh].cpu().numpy(), d).reshape(T * 64, d)
+    assert np.array_equal(q8, prep.q8)
+    assert np.array_equal(k8, prep.k8)
+    assert np.array_equal(g["DQ"].view(np.uint32), prep.dq.view(np.uint32))
+    assert np.array_equal(g["DK"].view(np.uint32), prep.dk.view(np.uint32))
+    return prep
+
+
+def compare_blocks(o_head, wl, Qh, Kh, Vh, W, prep, blocks, sm_scale=None):
+    res = oracle.head_forward(Qh, Kh, Vh, W, float(np.float32(wl.topk)),
+                              use_linear=bool(wl.use_linear), blocks=blocks, prep=prep,
+                              sm_scale=sm_scale)
+    got, ref = [], []
+    for i in blocks:
+        n = res[i].shape[0]
+        got.append(f32(o_head[64 * i:64 * i + n]))
+        ref.append(res[i])
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    return got, ref
+
+
+def assert_close(got, ref, label):
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    rms = float(np.sqrt((ref ** 2).mean())) if ref.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    say(f"[parity] {label}: max-abs {mx:.3e} rel-L2 {rel:.3e} max-abs/rms {mx / max(rms, 1e-300):.3e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= MAX_ABS
+    if np.linalg.norm(ref) > 0:
+        assert rel <= REL_L2
+    else:
+        assert mx == 0.0
+
+
+def full_compare(wl, sm_scale=0.0):
+    m, o, dv, inputs = run(wl, sm_scale=sm_scale)
+    q, k, v, w = inputs
+    out = host_u16(o)
+    scale = sm_scale if sm_scale > 0 else None
+    G, R = [], []
+    for b, h in wl.heads():
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h])
+        got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep,
+                                  list(range(m.plan.info.T)), sm_scale=scale)
+        G.append(got)
+        R.append(ref)
+    assert_close(np.concatenate(G), np.concatenate(R), wl.name)
+    return m, o, dv, inputs
+
+
+SMALL = [
+    synth.Workload("tiny", 1, 2, 1024, 64, 0.25),
+    synth.Workload("tiny-d128-ragged", 1, 2, 1000, 128, 0.25),
+    synth.Workload("two-blocks", 1, 1, 65, 64, 0.5),
+    synth.Workload("one-token", 1, 1, 1, 128, 0.1),
+    synth.Workload("pure-linear", 1, 2, 700, 128, 0.0),
+    synth.Workload("all-kept-linear-on", 1, 1, 640, 128, 1.0),
+    synth.Workload("sparse-only-b2", 2, 1, 2000, 128, 0.3, use_linear=0),
+    synth.Workload("dense-outlier-small", 1, 2, 2048, 128, 1.0, use_linear=0, koff_std=4.0,
+                   outlier_frac=0.01, outlier_scale=20.0),
+    synth.Workload("preview-topk", 1, 1, 4000, 128, 0.05, seed=5),
+    synth.Workload("quality-topk", 1, 1, 4000, 64, 0.15, seed=6),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_parity(wl):
+    full_compare(wl)
+
+
+def test_explicit_sm_scale():
+    full_compare(synth.Workload("scale", 1, 1, 777, 128, 0.2, seed=9), sm_scale=0.05)
+
+
+def test_int32_qk_tiles_bit_exact():
+    wl = synth.Workload("qk", 1, 2, 1000, 128, 0.5, seed=2)
+    m, o, dv, (q, k, v, w) = run(wl)
+    T = m.plan.info.T
+    triples = [(0, 0, 0), (0, 3, 15), (1, 15, 15), (1, 7, 2), (0, 15, 0)]
+    tiles = m.debug_qk_int32(triples).cpu().numpy()
+    for n, (bh, i, j) in enumerate(triples):
+        prep = oracle.head_prep(q[0, bh], k[0, bh], float(np.float32(wl.topk)))
+        ref = oracle.qk_int32(prep.q8, prep.k8, i, j)
+        assert np.array_equal(tiles[n], ref), (bh, i, j)
+    bad = m.debug_qk_int32([(5, 0, 0), (0, T, 0)]).cpu().numpy()
+    assert np.all(bad == 0)
+
+
+def test_deterministic_reruns():
+    wl = synth.Workload("det", 1, 2, 3000, 128, 0.1, seed=4)
+    m, o1, dv, inputs = run(wl)
+    o2 = m(*dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_value_scaling_by_power_of_two_is_exact():
+    wl = synth.Workload("scale2", 1, 2, 1500, 128, 0.2, seed=8)
+    m, o1, (Q, K, V, W), _ = run(wl)
+    o2 = m(Q, K, (V.float() * 4.0).to(torch.bfloat16), W)
+    torch.cuda.synchronize()
+    assert torch.equal((o1.float() * 4.0).to(torch.bfloat16).view(torch.int16), o2.view(torch.int16))
+
+
+def test_head_permutation_equivariance():
+    wl = synth.Workload("perm", 1, 3, 1300, 64, 0.25, seed=7)
+    m, o, (Q, K, V, W), _ = run(wl)
+    perm = [2, 0, 1]
+    o2 = m(Q[:, perm].contiguous(), K[:, perm].contiguous(), V[:, perm].contiguous(), W)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, perm].contiguous().view(torch.int16), o2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- full size ---
+
+BIG = ["wan1.3b-480p", "wan14b-480p", "wan14b-720p", "dense-outlier"]
+
+
+def mask_properties(m):
+    """Every row of every head keeps exactly kb blocks, listed ascending."""
+    T, kb = m.plan.info.T, m.plan.info.kb
+    words = m.region("MASK")
+    cnt = torch.zeros(words.shape[:2], dtype=torch.int64, device=words.device)
+    for b in range(64):
+        cnt += ((words >> b) & 1).sum(-1)
+    assert bool((cnt == kb).all())
+    kept = m.region("KEPT")
+    if kb > 1:
+        assert bool((kept[:, :, 1:] > kept[:, :, :-1]).all())
+    if kb:
+        assert bool((kept[:, :, 0] >= 0).all()) and bool((kept[:, :, -1] < T).all())
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_full_size_sampled_parity(name):
+    wl = synth.WORKLOADS[name]
+    say(f"[gpu] generating {name}")
+    inputs = synth.all_inputs(wl)
+    m, o, dv, _ = run(wl, inputs=inputs)
+    mask_properties(m)
+    assert bool(torch.isfinite(o.float()).all())
+    q, k, v, w = inputs
+    out = host_u16(o)
+    T = m.plan.info.T
+    blocks = sorted({0, 1, T // 2, T - 1})
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    G, R = [], []
+    for b, h in heads:
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h])
+        got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep, blocks)
+        G.append(got)
+        R.append(ref)
+        bh = b * wl.H + h
+        pairs = [(bh, i, int(prep.kept[i][0])) for i in blocks if prep.kept.shape[1]]
+        tiles = m.debug_qk_int32(pairs).cpu().numpy()
+        for n, (_, i, j) in enumerate(pairs):
+            assert np.array_equal(tiles[n], oracle.qk_int32(prep.q8, prep.k8, i, j))
+    assert_close(np.concatenate(G), np.concatenate(R), name)
