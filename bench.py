@@ -1,0 +1,233 @@
+"""SageSLA forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b-720p]
+
+One step = the whole forward (sla_quantize, then sla_prepare_kv and
+sla_attend) over one batch of seeded synthetic inputs already resident in
+HBM.  Prints one JSON line: dense-equivalent TFLOP/s (4*B*H*N^2*d per call /
+time), ms per call, the per-stage times, the roofline of the dominant kernel
+(the block-sparse attention kernel, timed with HIP events on the stream it
+runs on) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_bit_attention_amd import synth  # noqa: E402
+
+# MI355X published peaks
+P_I8 = 5.0e15        # dense INT8 MFMA, ops/s
+P_BF16 = 2.5e15      # dense bf16 MFMA, flop/s
+P_HBM = 8.0e12       # bytes/s
+METRIC = "SageSLA fwd ms/call + dense-equiv TFLOPS (%MFMA peak), Wan-14B-720P shape"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_wan14b-720p_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_bit_attention_amd", "csrc", "k_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_work(wl, kb, T):
+    """Algorithmic MFMA work of one launch of the attention kernel.
+
+    Per kept (query block, key block) pair: 2*64*64*d INT8 ops (QK^T) and
+    2*64*64*d bf16 flops (PV).  Per query block with the linear branch on:
+    2*64*d*d (H^T phi(Q)^T) + 2*64*d*d (projection) bf16 flops."""
+    BH = wl.B * wl.H
+    pairs = BH * T * kb
+    i8 = pairs * 2 * 64 * 64 * wl.d
+    bf = pairs * 2 * 64 * 64 * wl.d
+    if wl.use_linear and kb < T:
+        bf += BH * T * 4 * 64 * wl.d * wl.d
+    return i8, bf, pairs
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_entry():
+    """HBM bytes per launch of the attention kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, n_blocks, log_fn=log):
+    """The oracle, single threaded, on one head of the workload: the head's
+    whole selection/quantisation and linear states plus n_blocks query blocks;
+    the head time is extrapolated to all T query blocks and reported as
+    dense-equivalent TFLOP/s (heads are independent and cost the same)."""
+    import oracle
+    q, k, v = synth.head_inputs(wl, 0, 0)
+    w = synth.proj_weight(wl)
+    T = oracle.nblocks(wl.N)
+    t0 = time.perf_counter()
+    prep = oracle.head_prep(q, k, float(np.float32(wl.topk)))
+    states = oracle.linear_states(k, v) if wl.use_linear else None
+    t1 = time.perf_counter()
+    rng = np.random.default_rng(0)
+    blocks = sorted(rng.choice(T, size=min(n_blocks, T), replace=False).tolist())
+    oracle.head_forward(q, k, v, w, float(np.float32(wl.topk)), use_linear=bool(wl.use_linear),
+                        blocks=blocks, prep=prep, states=states)
+    t2 = time.perf_counter()
+    head_s = (t1 - t0) + (t2 - t1) * T / len(blocks)
+    dense = 4.0 * wl.N * wl.N * wl.d
+    log_fn(f"[cpu] prep+states {t1 - t0:.2f}s, {len(blocks)} blocks {t2 - t1:.2f}s, "
+           f"head extrapolated {head_s:.1f}s")
+    return {
+        "value": dense / head_s / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"head (0,0) of {wl.name}: selection, quantisation and linear states for "
+                   f"the whole head ({t1 - t0:.1f}s) plus {len(blocks)} of {T} query blocks "
+                   f"({t2 - t1:.1f}s), extrapolated to the head ({head_s:.0f}s); "
+                   f"single thread, {platform.processor() or platform.machine()}"),
+        "ms_per_call_extrapolated": head_s * wl.B * wl.H * 1e3,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan14b-720p", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-blocks", type=int, default=360,
+                    help="query blocks the CPU oracle baseline computes (0 = skip)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_bit_attention_amd import sla
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
+        return
+
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {wl.name} inputs")
+    t0 = time.perf_counter()
+    q, k, v, w = synth.all_inputs(wl)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V, W = up(q), up(k), up(v), up(w)
+    del q, k, v
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+    m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear), device=dev)
+    T, kb = m.plan.info.T, m.plan.info.kb
+    out = torch.empty_like(Q)
+    Wp = W if wl.use_linear else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m.quantize(Q, K, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        m.prepare_kv(K, V, Wp, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        m.attend(Q, out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    st = np.array([[e[a].elapsed_time(e[a + 1]) for a in range(3)] for e in events])  # ms
+    ms_step = wall * 1e3 / args.steps
+    q_ms, kv_ms, at_ms = (float(np.mean(st[:, a])) for a in range(3))
+    log(f"[bench] ms/step {ms_step:.3f} (quantize {q_ms:.3f}, prepare_kv {kv_ms:.3f}, "
+        f"attend {at_ms:.3f})")
+
+    dense = 4.0 * wl.B * wl.H * wl.N * wl.N * wl.d
+    i8, bf, pairs = attn_work(wl, kb, T)
+    # the MFMA roofline time of the kept-block work: int8 and bf16 share the units
+    t_roof_kept = (pairs * 2 * 64 * 64 * wl.d) / P_I8 + (pairs * 2 * 64 * 64 * wl.d) / P_BF16
+    t_roof_attn = i8 / P_I8 + bf / P_BF16
+    blended_peak = (i8 + bf) / t_roof_attn
+    achieved = (i8 + bf) / (at_ms * 1e-3)
+    traffic = traffic_entry()
+
+    res = {
+        "metric": METRIC,
+        "value": dense / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "block": 64,
+                   "topk": wl.topk, "kb": kb, "use_linear": wl.use_linear},
+        "ms_per_call": ms_step,
+        "stage_ms": {"sla_quantize": q_ms, "sla_prepare_kv": kv_ms, "sla_attend": at_ms},
+        "pct_mfma_roofline_kept_blocks": 100.0 * t_roof_kept / (ms_step * 1e-3),
+        "roofline": {
+            "kernel": "k_attn (sla_attend)",
+            "bound": "mfma",
+            "achieved": achieved / 1e12,
+            "peak": blended_peak / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / blended_peak,
+            "traffic": traffic,
+        },
+    }
+    if args.cpu_blocks > 0:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,6 +98,18 @@ sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, cons
                              const void *w_proj, void *out, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* The two stages of sla_attention_fwd, for callers that schedule or time
+ * them separately (same arguments, same order on one stream):
+ * sla_prepare_kv: V re-layout, per key block linear states and the marginal
+ *   states per query block (the last two only when the linear branch is on);
+ * sla_attend: the block-sparse attention kernel with the linear branch and
+ *   projection in its epilogue, writing out.
+ * Needs sla_quantize first; sla_attend needs sla_prepare_kv first. */
+sla_status sla_prepare_kv(sla_plan_t plan, const void *k, const void *v, const void *w_proj,
+                          void *ws, size_t ws_bytes, void *stream);
+sla_status sla_attend(sla_plan_t plan, const void *q, void *out, void *ws, size_t ws_bytes,
+                      void *stream);
+
 /* Static text for a status code. */
 const char *sla_status_string(sla_status s);
 

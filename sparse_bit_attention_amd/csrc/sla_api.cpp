@@ -181,13 +181,12 @@ sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
   return launched();
 }
 
-sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
-                             const void *w_proj, void *out, void *ws, size_t ws_bytes,
-                             void *stream) {
-  if (!plan || !q || !k || !v || !out) return SLA_EINVAL;
+sla_status sla_prepare_kv(sla_plan_t plan, const void *k, const void *v, const void *w_proj,
+                          void *ws, size_t ws_bytes, void *stream) {
+  if (!plan || !k || !v) return SLA_EINVAL;
   const Plan &p = plan->p;
   if (p.cfg.use_linear && !w_proj) return SLA_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SLA_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16)) return SLA_EINVAL;
   if (w_proj && !aligned(w_proj, 16)) return SLA_EINVAL;
   sla_status s = check_ws(p, ws, ws_bytes);
   if (s != SLA_OK) return s;
@@ -199,8 +198,34 @@ sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, cons
     launch_w_swizzle(p, (const uint16_t *)w_proj, w, st);
     launch_marginal(p, w, st);
   }
-  launch_attn(p, (const uint16_t *)q, w, (uint16_t *)out, st);
   return launched();
+}
+
+sla_status sla_attend(sla_plan_t plan, const void *q, void *out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!plan || !q || !out) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SLA_EINVAL;
+  sla_status s = check_ws(p, ws, ws_bytes);
+  if (s != SLA_OK) return s;
+  (void)hipGetLastError();
+  launch_attn(p, (const uint16_t *)q, ws_ptrs(p, ws), (uint16_t *)out, (hipStream_t)stream);
+  return launched();
+}
+
+sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
+                             const void *w_proj, void *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  if (!plan || !q || !k || !v || !out) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (p.cfg.use_linear && !w_proj) return SLA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SLA_EINVAL;
+  if (w_proj && !aligned(w_proj, 16)) return SLA_EINVAL;
+  sla_status s = check_ws(p, ws, ws_bytes);
+  if (s != SLA_OK) return s;
+  s = sla_prepare_kv(plan, k, v, w_proj, ws, ws_bytes, stream);
+  if (s != SLA_OK) return s;
+  return sla_attend(plan, q, out, ws, ws_bytes, stream);
 }
 
 sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr, size_t *bytes) {

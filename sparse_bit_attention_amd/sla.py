@@ -17,7 +17,8 @@ SLA_OK, SLA_EINVAL, SLA_EUNSUPPORTED, SLA_EWORKSPACE, SLA_EHIP, SLA_ENOMEM = ran
 WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "DK"]
 
 EXPORTS = ["sla_plan", "sla_plan_destroy", "sla_plan_info", "sla_quantize", "sla_attention_fwd",
-           "sla_status_string", "sla_ws_view", "sla_debug_qk_int32"]
+           "sla_prepare_kv", "sla_attend", "sla_status_string", "sla_ws_view",
+           "sla_debug_qk_int32"]
 
 
 class SlaError(RuntimeError):
@@ -54,6 +55,10 @@ def lib():
         L.sla_quantize.restype = ctypes.c_int
         L.sla_attention_fwd.argtypes = [P, P, P, P, P, P, P, sz, P]
         L.sla_attention_fwd.restype = ctypes.c_int
+        L.sla_prepare_kv.argtypes = [P, P, P, P, P, sz, P]
+        L.sla_prepare_kv.restype = ctypes.c_int
+        L.sla_attend.argtypes = [P, P, P, P, sz, P]
+        L.sla_attend.restype = ctypes.c_int
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
         L.sla_ws_view.argtypes = [P, P, i32, ctypes.POINTER(P), ctypes.POINTER(sz)]
@@ -153,6 +158,24 @@ class SageSLA:
                                        self._tensor(out, "out", self.shape),
                                        ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
                                        self._stream(stream)), "sla_attention_fwd")
+        return out
+
+    def prepare_kv(self, k, v, w=None, stream=None):
+        d = self.shape[3]
+        wp = self._tensor(w, "w", (d, d)) if w is not None else ctypes.c_void_p(0)
+        _check(lib().sla_prepare_kv(self.plan.handle, self._tensor(k, "k", self.shape),
+                                    self._tensor(v, "v", self.shape), wp,
+                                    ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                    self._stream(stream)), "sla_prepare_kv")
+
+    def attend(self, q, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(self.shape, dtype=torch.bfloat16, device=self.device)
+        _check(lib().sla_attend(self.plan.handle, self._tensor(q, "q", self.shape),
+                                self._tensor(out, "out", self.shape),
+                                ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                self._stream(stream)), "sla_attend")
         return out
 
     def forward(self, q, k, v, w=None, out=None, stream=None):
