@@ -20,16 +20,25 @@
 // Epilogue: O_l^T = H_i^T phi(Q_i)^T / (phi(Q_i) . z_i), then
 // O^T += W O_l^T, all bf16 MFMA into the same accumulators, bf16 store.
 //
+// Memory: each wave owns 40 KiB of LDS, one K8 slot (8 KiB) and two V slots
+// (16 KiB each).  The fragments of key block n+1 are copied global -> LDS
+// (16-byte direct loads, no VGPRs) while block n is computed, so every load has
+// a whole block of work to land.  On gfx950 MFMA and VALU time add up rather
+// than overlap, so the softmax keeps its per-score work to convert, FMA, exp2,
+// half a pack and half a dot2, and padding keys are not masked per element:
+// their exactly known contribution is subtracted from the row sum.
+//
 // MFMA work per kept pair (d = 128): 2*64*64*128 int8 ops + as many bf16
-// flops; K8 (8 KiB) and V (16 KiB) fragments are loaded straight into
-// registers with 16-byte lane loads (fragment order in memory), prefetched one
-// key block ahead.
+// flops.
 #include "sla_internal.h"
 
 namespace sla {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
+// Largest per-row logit bound (log2 units) for which exp2(logit - bound) keeps
+// the row's largest probabilities far from float32 underflow.
+constexpr float BOUND_LIMIT = 64.0f;
 
 template <int D>
 __device__ __forceinline__ void load_q8(const int8_t *q8blk, v4i (&qf)[4][D / 64], int lane) {
@@ -56,17 +65,166 @@ __device__ __forceinline__ void qk_int8(const v4i (&kf)[4][D / 64], const v4i (&
     }
 }
 
-template <int D, bool LIN>
+// s_waitcnt with only vmcnt = 0 (expcnt, lgkmcnt left at their maxima)
+#define SLA_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
+// s_waitcnt with only lgkmcnt = 0
+#define SLA_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Copy nfrag 1 KiB fragments global -> LDS; lane l moves bytes [16l, 16l+16)
+// of each fragment, which land at the same offsets in LDS.
+__device__ __forceinline__ void dma_frags(const uint4 *src, uint4 *dst, int nfrag, int lane) {
+  for (int f = 0; f < nfrag; ++f)
+    __builtin_amdgcn_global_load_lds((gbl_void *)(src + f * 64 + lane), (lds_void *)(dst + f * 64), 16,
+                                     0, 0);
+}
+
+// Probabilities of one 32-key half for query tile U as a bf16 B fragment (k
+// order of kmaj_off) and their sum: p = exp2(score * c - m).
+template <int U>
+__device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m, float &lsum) {
+  const float nm = -m;
+  const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
+  // The pairs stay in scalars: bit-casting an element of an ext-vector is
+  // miscompiled by this clang (every element reads element 0).
+  uint32_t pk[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int e0 = 2 * h, e1 = 2 * h + 1;
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[e0 >> 2][U][e0 & 3], c, nm));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[e1 >> 2][U][e1 & 3], c, nm));
+    pk[h] = pack2bf(x0, x1);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[h]), one, lsum, false);
+  }
+  return v4u{pk[0], pk[1], pk[2], pk[3]};
+}
+
+// The kept-block loop, each key block in two 32-key halves
+// (QK^T half -> probabilities -> PV half).  BOUND: m is an upper bound of
+// every logit of the row (set before the loop): no running max, no rescaling.
+// Otherwise m is a running max, moved lazily per half.
+template <int D, bool BOUND>
+__device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D / 16][4],
+                                          float (&m)[4], float (&lsum)[4], const int32_t *kl,
+                                          int kb, const float *dk, const uint4 *k8u,
+                                          const uint4 *vtu, size_t headblk, float dqi, int T,
+                                          int npad_lane, uint4 *kslot, uint4 *vslot0, int lane) {
+  constexpr int KC = D / 64, CG = D / 16;
+  constexpr int KFR = 64 * D / 1024;
+  constexpr int VFR = 2 * 64 * D / 1024;
+  if (kb > 0) {
+    const int j0 = kl[0];
+    dma_frags(k8u + (headblk + j0) * KFR * 64, kslot, KFR, lane);
+    dma_frags(vtu + (headblk + j0) * VFR * 64, vslot0, VFR, lane);
+  }
+  for (int n = 0; n < kb; ++n) {
+    const int j = kl[n];
+    const float c = dqi * dk[headblk + j];
+    const uint4 *vcur = vslot0 + (n & 1) * VFR * 64;
+    // block n's K8 and V are in LDS once every outstanding copy has landed
+    SLA_WAIT_VMCNT0();
+    __builtin_amdgcn_sched_barrier(0);
+    v4i kf[4][KC];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[t][kc] = __builtin_bit_cast(v4i, kslot[(t * KC + kc) * 64 + lane]);
+    SLA_WAIT_LGKMCNT0();
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 1 < kb) {
+      const int jn = kl[n + 1];
+      dma_frags(k8u + (headblk + jn) * KFR * 64, kslot, KFR, lane);
+      dma_frags(vtu + (headblk + jn) * VFR * 64, vslot0 + ((n + 1) & 1) * VFR * 64, VFR, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // S^T for key tiles 2hf, 2hf+1
+      v4i s[2][4];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v4i acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(kf[2 * hf + t2][kc], qf[u][kc], acc);
+          s[t2][u] = acc;
+        }
+      if (!BOUND) {
+        // half-tile max per query (padding keys score 0 and may only raise it)
+        int imax[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int a0 = max(max(s[0][u][0], s[0][u][1]), s[0][u][2]);
+          const int a1 = max(max(s[0][u][3], s[1][u][0]), s[1][u][1]);
+          imax[u] = max(max(a0, a1), max(s[1][u][2], s[1][u][3]));
+        }
+        bool need = false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) need |= ((float)imax[u] * c > m[u] + RESCALE_SLACK);
+        if (__ballot(need) != 0ull) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float tm = (float)imax[u] * c;
+            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+            if (tm > m[u] + RESCALE_SLACK) {
+              const float alpha = __builtin_amdgcn_exp2f(m[u] - tm);
+              m[u] = tm;
+              lsum[u] *= alpha;
+#pragma unroll
+              for (int a = 0; a < CG; ++a) o[a][u] *= alpha;
+            }
+          }
+        }
+      }
+      v4u pf[4];
+      pf[0] = probs_half<0>(s, c, m[0], lsum[0]);
+      pf[1] = probs_half<1>(s, c, m[1], lsum[1]);
+      pf[2] = probs_half<2>(s, c, m[2], lsum[2]);
+      pf[3] = probs_half<3>(s, c, m[3], lsum[3]);
+      v4u vf[CG];
+#pragma unroll
+      for (int a = 0; a < CG; ++a) vf[a] = __builtin_bit_cast(v4u, vcur[(hf * CG + a) * 64 + lane]);
+#pragma unroll
+      for (int a = 0; a < CG; ++a)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[a][u] = mfma_bf16(vf[a], pf[u], o[a][u]);
+    }
+    if (j == T - 1 && npad_lane > 0) {
+      // padding keys have score 0: remove exactly what the row sums received
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(-m[u]), 0.f);
+        lsum[u] -= (float)npad_lane * bf2f((uint16_t)(pp & 0xFFFF));
+      }
+    }
+  }
+}
+
+// BOUND = true: the main launch.  A query block whose logit bound exceeds
+// BOUND_LIMIT is only flagged (flags[qb] = 1) and left to the second launch,
+// BOUND = false, which runs the online-max loop for flagged blocks only.
+template <int D, bool LIN, bool BOUND>
 __global__ __launch_bounds__(256, 1) void k_attn(
     const int8_t *__restrict__ q8, const int8_t *__restrict__ k8, const float *__restrict__ dq,
-    const float *__restrict__ dk, const uint16_t *__restrict__ vt,
+    const float *__restrict__ dk, const float *__restrict__ dkn, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
-    int N, int T, int kb, int nqb, int F, float qk_scale) {
+    int32_t *__restrict__ flags, int N, int T, int kb, int nqb, int F, float qk_scale) {
   constexpr int KC = D / 64, CG = D / 16, KC32 = D / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int KFR = 64 * D / 1024;      // 1 KiB fragments per K8 block
+  constexpr int VFR = 2 * 64 * D / 1024;  // 1 KiB fragments per V block
+  constexpr int SLOT = (KFR + 2 * VFR) * 64;  // uint4 per wave
+  __shared__ uint4 ring[4][SLOT];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-  if (qb >= nqb) return;
+  if (qb >= nqb) return;  // no barriers below: waves are independent
+  if (!BOUND && flags[qb] == 0) return;
   const int bh = qb / T, i = qb - bh * T;
   const int g = lane >> 4, l16 = lane & 15;
   const int nlast = N - (T - 1) * BLK;
@@ -81,127 +239,66 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 #pragma unroll
     for (int u = 0; u < 4; ++u) o[a][u] = v4f{0.f, 0.f, 0.f, 0.f};
   float m[4], lsum[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    m[u] = -INFINITY;
-    lsum[u] = 0.f;
-  }
 
   const int32_t *kl = kept + (size_t)qb * kb;
   const size_t headblk = (size_t)bh * T;
+  // padding keys of the last block held by this lane (keys 16t + 4g + r >= nlast)
+  int npad_lane = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) npad_lane += (16 * t + 4 * g + r) >= nlast;
 
-  // K8 of the next key block is fetched right after this block's QK^T, V of
-  // the next block right after this block's PV product.
-  v4i kf[4][KC];
-  v4u vf[2][CG];
-  auto load_k = [&](int j) {
-    const v4i *kp = (const v4i *)(k8 + (headblk + j) * BLK * D);
+  // Upper bound of the row's logits (log2 units): |q8_r . k8_s| <= ||q8_r||
+  // ||k8_s||, so logit <= dq_i sm_scale log2(e) ||q8_r|| max_j (dk_j max_s ||k8_s||).
+  float kmax = 0.f;
+  for (int n = 0; n < kb; ++n) kmax = fmaxf(kmax, dkn[headblk + kl[n]]);
+  bool bounded = true;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int u = 0; u < 4; ++u) {
+    int sq = 0;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) kf[t][kc] = kp[(t * KC + kc) * 64 + lane];
-  };
-  auto load_v = [&](int j) {
-    const v4u *vp = (const v4u *)(vt + (headblk + j) * BLK * D);
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2)
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wv = (uint32_t)qf[u][kc][e];
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg) vf[kc2][cg] = vp[(kc2 * CG + cg) * 64 + lane];
-  };
-
-  int jn = kb > 0 ? kl[0] : 0;
-  if (kb > 0) {
-    load_k(jn);
-    load_v(jn);
-  }
-  for (int n = 0; n < kb; ++n) {
-    const int j = jn;
-    const float c = dqi * dk[headblk + j];
-    v4i s[4][4];
-    qk_int8<D>(kf, qf, s);
-    if (n + 1 < kb) {
-      jn = kl[n + 1];
-      load_k(jn);
-    }
-    // keys past N in the last block are excluded
-    const bool tail = (j == T - 1) && (nlast < BLK);
-    int imax[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int mx = INT_MIN;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * t + 4 * g + r;
-          const int v = (!tail || key < nlast) ? s[t][u][r] : INT_MIN;
-          mx = max(mx, v);
-        }
-      imax[u] = mx;
-    }
-    // lazy running max: move it only when a tile exceeds it by the slack
-    bool need = false;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) need |= ((float)imax[u] * c > m[u] + RESCALE_SLACK);
-    if (__ballot(need) != 0ull) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float tm = (float)imax[u] * c;
-        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-        if (tm > m[u] + RESCALE_SLACK) {
-          const float alpha = __builtin_amdgcn_exp2f(m[u] - tm);
-          m[u] = tm;
-          lsum[u] *= alpha;
-#pragma unroll
-          for (int a = 0; a < CG; ++a) o[a][u] *= alpha;
+        for (int b8 = 0; b8 < 4; ++b8) {
+          const int v8 = (int)(int8_t)(wv >> (8 * b8));
+          sq += v8 * v8;
         }
       }
-    }
-    // probabilities -> bf16 B fragments (k order of kmaj_off), row sums
-    v4u pf[2][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float nm = -m[u];
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = 2 * kc2 + (e >> 2), r = e & 3;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][u][r], c, nm));
-          if (tail && (16 * t + 4 * g + r) >= nlast) x = 0.f;
-          p[e] = x;
-        }
-        // The pairs stay in scalars: bit-casting an element of an ext-vector
-        // is miscompiled by this clang (every element reads element 0).
-        uint32_t pk[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) pk[h] = pack2bf(p[2 * h], p[2 * h + 1]);
-        pf[kc2][u] = v4u{pk[0], pk[1], pk[2], pk[3]};
-        const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          lsum[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[h]), one, lsum[u], false);
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < CG; ++a)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) o[a][u] = mfma_bf16(vf[kc2][a], pf[kc2][u], o[a][u]);
-    if (n + 1 < kb) load_v(jn);
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    m[u] = dqi * (sqrtf((float)sq) * (1.0f + 0x1p-20f)) * kmax;
+    lsum[u] = 0.f;
+    bounded = bounded && (m[u] <= BOUND_LIMIT);
   }
-  // normalise the sparse branch
+  uint4 *kslot = ring[w];
+  uint4 *vslot0 = ring[w] + KFR * 64;
+  if (BOUND) {
+    const bool fail = __ballot(!bounded) != 0ull;
+    if (lane == 0) flags[qb] = fail ? 1 : 0;
+    if (fail) return;
+    kept_loop<D, true>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
+                       dqi, T, npad_lane, kslot, vslot0, lane);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m[u] = -INFINITY;
+    kept_loop<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
+                        dqi, T, npad_lane, kslot, vslot0, lane);
+  }
+  // Row sums; O is normalised only while it is stored, so the accumulators
+  // are not touched by vector ALU code in between (they stay in AGPRs).
+  float linv[4], lrow[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float l = lsum[u];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-    for (int a = 0; a < CG; ++a) o[a][u] *= inv;
+    // no kept key (kb = 0): O is zero, and l = 1 leaves the linear branch as is
+    lrow[u] = l > 0.f ? l : 1.0f;
+    linv[u] = 1.0f / lrow[u];
   }
 
   if (LIN) {
@@ -246,14 +343,14 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       for (int kc = 0; kc < KC32; ++kc) {
         uint4 zv = *(const uint4 *)(hp + D * D + 32 * kc + 8 * g);
         const uint32_t zz[4] = {zv.x, zv.y, zv.z, zv.w};
-        v4u f;
+        uint32_t pk[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          f[h] = pack2bf(x[kc][2 * h] * rs, x[kc][2 * h + 1] * rs);
-          dd = __builtin_fmaf(bf2f((uint16_t)(f[h] & 0xFFFF)), bf2f((uint16_t)(zz[h] & 0xFFFF)), dd);
-          dd = __builtin_fmaf(bf2f((uint16_t)(f[h] >> 16)), bf2f((uint16_t)(zz[h] >> 16)), dd);
+          pk[h] = pack2bf(x[kc][2 * h] * rs, x[kc][2 * h + 1] * rs);
+          dd = __builtin_fmaf(bf2f((uint16_t)(pk[h] & 0xFFFF)), bf2f((uint16_t)(zz[h] & 0xFFFF)), dd);
+          dd = __builtin_fmaf(bf2f((uint16_t)(pk[h] >> 16)), bf2f((uint16_t)(zz[h] >> 16)), dd);
         }
-        pq[u][kc] = f;
+        pq[u][kc] = v4u{pk[0], pk[1], pk[2], pk[3]};
       }
       dd += __shfl_xor(dd, 16, 64);
       dd += __shfl_xor(dd, 32, 64);
@@ -275,20 +372,20 @@ __global__ __launch_bounds__(256, 1) void k_attn(
         ol[x][u] = a;
       }
     }
-    // normalise, pack as B fragments (k = value channel, kmaj order) and
-    // project: O^T += W O_l^T
+    // B fragments of O_l^T * (l / den) (k = value channel, kmaj order), so
+    // that O += W (O_l^T l) keeps the sparse sum unnormalised: the final
+    // 1/l then yields O_s + O_l W^T.
     v4u ob[KC32][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float r = den[u] > 0.f ? 1.0f / den[u] : 0.f;
+      const float r = den[u] > 0.f ? lrow[u] / den[u] : 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC32; ++kc) {
-        v4u f;
-        f[0] = pack2bf(ol[2 * kc][u][0] * r, ol[2 * kc][u][1] * r);
-        f[1] = pack2bf(ol[2 * kc][u][2] * r, ol[2 * kc][u][3] * r);
-        f[2] = pack2bf(ol[2 * kc + 1][u][0] * r, ol[2 * kc + 1][u][1] * r);
-        f[3] = pack2bf(ol[2 * kc + 1][u][2] * r, ol[2 * kc + 1][u][3] * r);
-        ob[kc][u] = f;
+        const uint32_t f0 = pack2bf(ol[2 * kc][u][0] * r, ol[2 * kc][u][1] * r);
+        const uint32_t f1 = pack2bf(ol[2 * kc][u][2] * r, ol[2 * kc][u][3] * r);
+        const uint32_t f2 = pack2bf(ol[2 * kc + 1][u][0] * r, ol[2 * kc + 1][u][1] * r);
+        const uint32_t f3 = pack2bf(ol[2 * kc + 1][u][2] * r, ol[2 * kc + 1][u][3] * r);
+        ob[kc][u] = v4u{f0, f1, f2, f3};
       }
     }
 #pragma unroll
@@ -304,15 +401,17 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     }
   }
 
-  // store: lane holds query 16u + l16, channels 16a + 4g .. +3
+  // store O / l: lane holds query 16u + l16, channels 16a + 4g .. +3
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row = i * BLK + 16 * u + l16;
     if (row < N) {
       uint16_t *orow = out + ((size_t)bh * N + row) * D;
+      const float r = linv[u];
 #pragma unroll
       for (int a = 0; a < CG; ++a) {
-        uint2 v = make_uint2(pack2bf(o[a][u][0], o[a][u][1]), pack2bf(o[a][u][2], o[a][u][3]));
+        uint2 v = make_uint2(pack2bf(o[a][u][0] * r, o[a][u][1] * r),
+                             pack2bf(o[a][u][2] * r, o[a][u][3] * r));
         *(uint2 *)(orow + 16 * a + 4 * g) = v;
       }
     }
@@ -347,24 +446,31 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t *__restrict__ q8,
       for (int r = 0; r < 4; ++r) o[(16 * u + l16) * BLK + 16 * t + 4 * g + r] = s[t][u][r];
 }
 
-void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st) {
+template <int D, bool LIN>
+static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
+                          hipStream_t st) {
   const int nqb = p.BH * p.T;
   dim3 grid((nqb + 3) / 4), block(256);
   const float qk_scale = p.sm_scale * LOG2E;
+  hipLaunchKernelGGL((k_attn<D, LIN, true>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.dkn,
+                     ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb, p.F,
+                     qk_scale);
+  hipLaunchKernelGGL((k_attn<D, LIN, false>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.dkn,
+                     ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb, p.F,
+                     qk_scale);
+}
+
+void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st) {
   if (p.d == 128) {
     if (p.lin_on)
-      hipLaunchKernelGGL((k_attn<128, true>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.vt,
-                         ws.kept, q, ws.hi, ws.wsw, out, p.N, p.T, p.kb, nqb, p.F, qk_scale);
+      launch_attn_t<128, true>(p, q, ws, out, st);
     else
-      hipLaunchKernelGGL((k_attn<128, false>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.vt,
-                         ws.kept, q, ws.hi, ws.wsw, out, p.N, p.T, p.kb, nqb, p.F, qk_scale);
+      launch_attn_t<128, false>(p, q, ws, out, st);
   } else {
     if (p.lin_on)
-      hipLaunchKernelGGL((k_attn<64, true>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.vt,
-                         ws.kept, q, ws.hi, ws.wsw, out, p.N, p.T, p.kb, nqb, p.F, qk_scale);
+      launch_attn_t<64, true>(p, q, ws, out, st);
     else
-      hipLaunchKernelGGL((k_attn<64, false>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.vt,
-                         ws.kept, q, ws.hi, ws.wsw, out, p.N, p.T, p.kb, nqb, p.F, qk_scale);
+      launch_attn_t<64, false>(p, q, ws, out, st);
   }
 }
 

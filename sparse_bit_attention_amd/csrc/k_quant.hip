@@ -116,7 +116,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
                                                  const float *__restrict__ mu, int N, int T,
                                                  int nblk, int8_t *__restrict__ k8,
-                                                 float *__restrict__ dk) {
+                                                 float *__restrict__ dk, float *__restrict__ dkn) {
   constexpr int LPR = D / 4;       // lanes per row
   constexpr int RPI = 64 / LPR;    // rows per step
   constexpr int STEPS = BLK / RPI;
@@ -152,19 +152,31 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
   const float delta = (float)((double)amax / 127.0);
   const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
   if (live && l == 0) dk[blk] = delta;
+  int nmax = 0;  // max over rows of the squared L2 norm of the codes
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int r = s * RPI + r0;
     uint32_t packed = 0;
+    int sq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float y = __builtin_rintf(xs[s][e] * inv);
       y = fminf(fmaxf(y, -127.f), 127.f);
-      packed |= ((uint32_t)(uint8_t)(int8_t)(int)y) << (8 * e);
+      const int code = (int)y;
+      sq += code * code;
+      packed |= ((uint32_t)(uint8_t)(int8_t)code) << (8 * e);
     }
-    if (r >= n) packed = 0;
+    if (r >= n) packed = 0, sq = 0;
     *(uint32_t *)(&stage[w][i8_off(r, c0, KC)]) = packed;
+    // sum over the LPR lanes holding this row
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+    nmax = max(nmax, sq);
   }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off, 64));
+  // dk * max_s ||k8_s||: with ||q8_r|| it bounds every int32 score of the block
+  if (live && l == 0) dkn[blk] = delta * (sqrtf((float)nmax) * (1.0f + 0x1p-20f));
   __syncthreads();
   if (live) {
     const uint4 *src = (const uint4 *)stage[w];
@@ -194,9 +206,11 @@ void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStrea
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
   if (p.d == 128)
-    hipLaunchKernelGGL(k_quant_k<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk);
+    hipLaunchKernelGGL(k_quant_k<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk,
+                       ws.dkn);
   else
-    hipLaunchKernelGGL(k_quant_k<64>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk);
+    hipLaunchKernelGGL(k_quant_k<64>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk,
+                       ws.dkn);
 }
 
 }  // namespace sla

@@ -122,6 +122,7 @@ class Workload:
     outlier_frac: float = 0.0      # fraction of channels whose offset is scaled
     outlier_scale: float = 1.0
     seed: int = 0
+    q_std: float = 1.0             # Q ~ N(0, q_std**2) (sharper attention when > 1)
 
     @property
     def T(self) -> int:
@@ -167,7 +168,7 @@ def head_inputs(wl: Workload, b: int, h: int):
     """bf16 bits of Q, K, V for one head, each [N, d] (uint16)."""
     n = wl.N * wl.d
     start = (b * wl.H + h) * n
-    q = normal_bf16(wl.seed, TID_Q, n, start)
+    q = normal_bf16(wl.seed, TID_Q, n, start, std=wl.q_std)
     k = normal_bf16(wl.seed, TID_KNOISE, n, start, add=k_offsets(wl, b, h))
     v = normal_bf16(wl.seed, TID_V, n, start)
     return q.reshape(wl.N, wl.d), k.reshape(wl.N, wl.d), v.reshape(wl.N, wl.d)
@@ -182,7 +183,7 @@ def all_inputs(wl: Workload):
     """bf16 bits of Q, K, V as [B, H, N, d] and W as [d, d]."""
     shape = (wl.B, wl.H, wl.N, wl.d)
     n = wl.B * wl.H * wl.N * wl.d
-    q = normal_bf16(wl.seed, TID_Q, n)
+    q = normal_bf16(wl.seed, TID_Q, n, std=wl.q_std)
     offs = np.concatenate([k_offsets(wl, b, h) for b, h in wl.heads()])
     # offset of head e, channel c sits at offs[e * d + c]; flat index n of K
     # belongs to head n // (N d) and channel n % d.

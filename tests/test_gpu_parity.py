@@ -143,6 +143,10 @@ SMALL = [
                    outlier_frac=0.01, outlier_scale=20.0),
     synth.Workload("preview-topk", 1, 1, 4000, 128, 0.05, seed=5),
     synth.Workload("quality-topk", 1, 1, 4000, 64, 0.15, seed=6),
+    # logits ~6x sharper: the per-row logit bound exceeds its limit, so these
+    # query blocks go through the online-max attention launch
+    synth.Workload("sharp-online-max", 1, 2, 3000, 128, 0.2, seed=11, q_std=6.0),
+    synth.Workload("sharp-online-max-d64", 1, 1, 2000, 64, 0.3, seed=12, q_std=8.0),
 ]
 
 
