@@ -168,117 +168,153 @@ __global__ void k_w_swizzle(const uint16_t *__restrict__ W, int D, uint16_t *__r
   }
 }
 
-// Byte b -> 8 bf16 (bit e of b -> 1.0 or 0.0 at element e), as 4 dwords.
-__device__ __forceinline__ v4u expand_bits(uint32_t b) {
-  v4u r;
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    uint32_t lo = ((b >> (2 * h)) & 1u) ? 0x3F80u : 0u;
-    uint32_t hi = ((b >> (2 * h + 1)) & 1u) ? 0x3F800000u : 0u;
-    r[h] = lo | hi;
-  }
-  return r;
-}
+// H[i][f] = sum_j (1 - M[i][j]) Hb[j][f] for one head and a 32-column slice
+// of f, all query-block rows i at once (so each Hb element is read once per
+// head).  8 waves; wave w owns row tiles [MW*w, MW*w + MW) (16 rows each).
+// Per step of 64 key blocks j: the B slice (64 x 32 bf16) is staged in LDS
+// transposed to [f][j] so a lane's 8 consecutive j are one 16-byte read; the A
+// fragments come from the row's mask word through a 16-entry LDS table that
+// expands 4 complemented mask bits to 4 bf16 ones/zeros (8 bytes per entry:
+// the 16 entries sit in distinct banks, so lookups never conflict).
+constexpr int MARG_TN = 32;   // columns per workgroup
+constexpr int MARG_TK = 64;   // key blocks per step (one mask word)
+constexpr int MARG_MW = 10;   // row tiles per wave: 8 * 10 * 16 = 1280 rows per pass
 
-// H[i][f] = sum_j (1 - M[i][j]) Hb[j][f] for one head; 128 x 128 output tile
-// per workgroup, 4 waves in 2 x 2, 32 key blocks per step.  B rows are staged
-// through LDS transposed ([f][j]) so each lane reads its 8 consecutive j with
-// one 16-byte load.
 template <int D>
-__global__ __launch_bounds__(256) void k_marginal(const uint64_t *__restrict__ mask,
+__global__ __launch_bounds__(512) void k_marginal(const uint64_t *__restrict__ maskt,
                                                   const uint16_t *__restrict__ hb, int T, int W64,
                                                   int F, uint16_t *__restrict__ hi) {
-  constexpr int TM = 128, TN = 128, TK = 32;
-  constexpr int PB = TK + 8;  // bf16 pitch of the transposed B tile (16-byte aligned rows)
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TN * PB];
-  const int mtiles = (T + TM - 1) / TM, ntiles = F / TN;
-  int b = blockIdx.x;
-  const int nt0 = b % ntiles;
-  b /= ntiles;
-  const int mt0 = b % mtiles;
-  const int bh = b / mtiles;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int PB = MARG_TK + 8;  // bf16 pitch of the transposed B slice (16-byte rows)
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][MARG_TN * PB];
+  __shared__ __attribute__((aligned(16))) uint2 lut[16];
+  const int nslices = F / MARG_TN;
+  const int mpasses = (T + 8 * MARG_MW * 16 - 1) / (8 * MARG_MW * 16);
+  // consecutive column slices of a head share 128-byte Hb lines: keep them
+  // on one XCD
+  int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int ns = b % nslices;
+  b /= nslices;
+  const int mp = b % mpasses;
+  const int bh = b / mpasses;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-  const int i_base = mt0 * TM + wm, f_base = nt0 * TN;
-  const uint16_t *hbh = hb + (size_t)bh * T * F;
+  const int f_base = ns * MARG_TN;
+  const int row0 = mp * (8 * MARG_MW * 16) + w * (MARG_MW * 16);
+  const uint16_t *hbh = hb + (size_t)bh * T * F + f_base;
+  const uint64_t *mh = maskt + (size_t)bh * W64 * T;  // word-major: [W64][T]
 
-  v4f acc[4][4];
+  if (tid < 16) {
+    uint32_t v[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h)
+      v[h] = (((tid >> (2 * h)) & 1) ? 0x3F80u : 0u) | (((tid >> (2 * h + 1)) & 1) ? 0x3F800000u : 0u);
+    lut[tid] = make_uint2(v[0], v[1]);
+  }
 
-  // global -> register loads of one B step: 32 rows x 128 columns, two
-  // 16-byte pieces per thread
-  auto load_b = [&](int j0, uint4 (&r)[2]) {
+  v4f acc[MARG_MW][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int x = tid + 256 * q;
-      const int jr = x >> 4, c8 = (x & 15) * 8;
-      const int j = j0 + jr;
-      r[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < T) r[q] = *(const uint4 *)(hbh + (size_t)j * F + f_base + c8);
+  for (int a = 0; a < MARG_MW; ++a) {
+    acc[a][0] = v4f{0.f, 0.f, 0.f, 0.f};
+    acc[a][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // one B step: 64 rows j x 32 columns; thread t loads 4 columns of row t/8
+  const int bj = tid >> 3, bf4 = (tid & 7) * 4;
+  auto load_b = [&](int j0) -> uint2 {
+    const int j = j0 + bj;
+    uint2 v = make_uint2(0u, 0u);
+    if (j < T) v = *(const uint2 *)(hbh + (size_t)j * F + bf4);
+    return v;
+  };
+  auto store_b = [&](int buf, uint2 v) {
+    uint16_t *d = &sB[buf][bf4 * PB + bj];
+    d[0] = (uint16_t)(v.x & 0xFFFF);
+    d[PB] = (uint16_t)(v.x >> 16);
+    d[2 * PB] = (uint16_t)(v.y & 0xFFFF);
+    d[3 * PB] = (uint16_t)(v.y >> 16);
+  };
+
+  // mask words of this lane's rows, fetched one step ahead
+  auto load_words = [&](int st, uint64_t (&wd)[MARG_MW]) {
+#pragma unroll
+    for (int a = 0; a < MARG_MW; ++a) {
+      const int i = row0 + 16 * a + l16;
+      wd[a] = mh[(size_t)st * T + min(i, T - 1)];
     }
   };
-  auto store_b = [&](int buf, const uint4 (&r)[2]) {
+  // rows past T read a valid row and are then forced to "all kept" (A = 0)
+  uint64_t rowpad[MARG_MW];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int x = tid + 256 * q;
-      const int jr = x >> 4, c8 = (x & 15) * 8;
-      const uint32_t v[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sB[buf][(c8 + e) * PB + jr] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-    }
-  };
-
-  const int steps = (T + TK - 1) / TK;
-  uint4 rb[2];
-  load_b(0, rb);
+  for (int a = 0; a < MARG_MW; ++a) rowpad[a] = (row0 + 16 * a + l16) < T ? 0ull : ~0ull;
+  const int steps = (T + MARG_TK - 1) / MARG_TK;
+  uint64_t wnext[MARG_MW];
+  load_words(0, wnext);
+  uint2 rb = load_b(0);
   store_b(0, rb);
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    const int j0 = s * TK;
-    if (s + 1 < steps) load_b(j0 + TK, rb);
-    // A fragments from the mask: rows i, the 8 key blocks j0 + 8g .. +7
-    v4u af[4];
+    const int j0 = s * MARG_TK;
+    uint64_t wcur[MARG_MW];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int i = i_base + 16 * a + l16;
-      uint32_t byte = 0u;
-      if (i < T) {
-        const int jj = j0 + 8 * g;
-        const uint64_t word = mask[((size_t)bh * T + i) * W64 + (jj >> 6)];
-        uint32_t kept8 = (uint32_t)(word >> (jj & 63)) & 0xFFu;
-        const int valid = min(8, max(0, T - jj));
-        const uint32_t vmask = valid >= 8 ? 0xFFu : ((1u << valid) - 1u);
-        byte = (~kept8) & vmask;
-      }
-      af[a] = expand_bits(byte);
+    for (int a = 0; a < MARG_MW; ++a) wcur[a] = wnext[a];
+    if (s + 1 < steps) {
+      rb = load_b(j0 + MARG_TK);
+      load_words(s + 1, wnext);
     }
-    v4u bfr[4];
+    // key blocks j0 + 32kc + 8g + e past T must give A = 0: set their mask
+    // bits (kept) before complementing; only the last step is short
+    uint32_t pad[2] = {0u, 0u};
+    if (j0 + MARG_TK > T) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      bfr[c] = *(const v4u *)(&sB[buf][(wn + 16 * c + l16) * PB + 8 * g]);
+      for (int kc = 0; kc < 2; ++kc) {
+        const int n = T - (j0 + 32 * kc);
+        pad[kc] = n >= 32 ? 0u : (n <= 0 ? ~0u : (~0u << n));
+      }
+    }
+    v4u bfr[2][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(af[a], bfr[c], acc[a][c]);
+      for (int kc = 0; kc < 2; ++kc)
+        bfr[nt][kc] = *(const v4u *)(&sB[buf][(16 * nt + l16) * PB + 32 * kc + 8 * g]);
+    // all A fragments of the step first (one LDS wait), then the products
+    v4u af[MARG_MW][2];
+#pragma unroll
+    for (int a = 0; a < MARG_MW; ++a)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const uint32_t half = (uint32_t)((wcur[a] | rowpad[a]) >> (32 * kc)) | pad[kc];
+        const uint32_t nb = ~half;
+        const uint2 lo = lut[__builtin_amdgcn_ubfe(nb, 8 * g, 4)];
+        const uint2 hi4 = lut[__builtin_amdgcn_ubfe(nb, 8 * g + 4, 4)];
+        af[a][kc] = v4u{lo.x, lo.y, hi4.x, hi4.y};
+      }
+#pragma unroll
+    for (int a = 0; a < MARG_MW; ++a)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        acc[a][0] = mfma_bf16(af[a][kc], bfr[0][kc], acc[a][0]);
+        acc[a][1] = mfma_bf16(af[a][kc], bfr[1][kc], acc[a][1]);
+      }
+    // issue order: index math, every LDS read, then the products
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * MARG_MW + 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MARG_MW, 0);
     if (s + 1 < steps) store_b(buf ^ 1, rb);
     __syncthreads();
   }
-  // store bf16 H rows i < T
-  uint16_t *hih = hi + (size_t)bh * T * F;
+  // store bf16 rows i < T: lane holds column 16nt + l16, rows 4g + r of each tile
+  uint16_t *hih = hi + (size_t)bh * T * F + f_base;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MARG_MW; ++a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i_base + 16 * a + 4 * g + r;
+      const int i = row0 + 16 * a + 4 * g + r;
       if (i < T) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) hih[(size_t)i * F + f_base + wn + 16 * c + l16] = f2bf(acc[a][c][r]);
+        hih[(size_t)i * F + l16] = f2bf(acc[a][0][r]);
+        hih[(size_t)i * F + 16 + l16] = f2bf(acc[a][1][r]);
       }
     }
 }
@@ -304,12 +340,13 @@ void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStr
 }
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
-  const int mtiles = (p.T + 127) / 128, ntiles = p.F / 128;
-  dim3 grid(p.BH * mtiles * ntiles), block(256);
+  const int nslices = p.F / MARG_TN;
+  const int mpasses = (p.T + 8 * MARG_MW * 16 - 1) / (8 * MARG_MW * 16);
+  dim3 grid(p.BH * mpasses * nslices), block(512);
   if (p.d == 128)
-    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.mask, ws.hb, p.T, p.W64, p.F, ws.hi);
+    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
   else
-    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, ws.mask, ws.hb, p.T, p.W64, p.F, ws.hi);
+    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
 }
 
 }  // namespace sla

@@ -102,11 +102,21 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
 }
 
 // mu[bh][c] = float32((sum over blocks t in order of ksum[bh][t][c]) / N).
+// Loads are issued 32 at a time ahead of the (ordered) additions.
 __global__ void k_kmean(const float *__restrict__ ksum, int N, int T, int D, float *__restrict__ mu) {
+  constexpr int BATCH = 32;
   const int bh = blockIdx.x, c = threadIdx.x;
   const float *p = ksum + (size_t)bh * T * D + c;
   float s = 0.f;
-  for (int t = 0; t < T; ++t) s = s + p[(size_t)t * D];
+  int t = 0;
+  for (; t + BATCH <= T; t += BATCH) {
+    float v[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) v[q] = p[(size_t)(t + q) * D];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) s = s + v[q];
+  }
+  for (; t < T; ++t) s = s + p[(size_t)t * D];
   mu[(size_t)bh * D + c] = (float)((double)s / (double)N);
 }
 

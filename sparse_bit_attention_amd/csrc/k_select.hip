@@ -24,14 +24,39 @@ __device__ __forceinline__ uint32_t score_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave selects row `srow` (T scores in LDS): mask words (W64 of them) and
-// the ascending kept list (kb entries).
-__device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, int32_t *krow,
-                           int lane) {
+// One wave selects one row: mask words (W64 of them) and the ascending kept
+// list (kb entries).  Lane l holds the keys of j = 64e + l, e < E.  CACHED:
+// the keys are in registers (E <= SEL_MAXE); otherwise every pass re-reads them
+// from LDS.
+constexpr int SEL_MAXE = 32;
+
+template <bool CACHED>
+struct RowKeys {
+  uint32_t k[CACHED ? SEL_MAXE : 1];
+  const float *srow;
+  int T, lane;
+  __device__ __forceinline__ uint32_t load(int e) const {
+    const int j = e * 64 + lane;
+    return j < T ? score_key(srow[j]) : 0u;  // 0 never equals a real key
+  }
+  __device__ __forceinline__ uint32_t get(int e) const {
+    if constexpr (CACHED) return k[e];
+    else return load(e);
+  }
+};
+
+template <bool CACHED>
+__device__ void select_row_t(const float *srow, int T, int kb, uint64_t *mrow, uint64_t *mcol,
+                             int32_t *krow, int lane) {
+  constexpr int EMAX = CACHED ? SEL_MAXE : (1 << 30);
   const int E = (T + 63) >> 6;
-  if (kb <= 0) {
-    for (int e = lane; e < E; e += 64) mrow[e] = 0ull;
-    return;
+  RowKeys<CACHED> rk;
+  rk.srow = srow;
+  rk.T = T;
+  rk.lane = lane;
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int e = 0; e < SEL_MAXE; ++e) rk.k[e] = e < E ? rk.load(e) : 0u;
   }
   // th = the kb-th largest key: the largest th with #{key >= th} >= kb,
   // built one bit at a time from the top.
@@ -39,25 +64,22 @@ __device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, int
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = th | (1u << bit);
     int cnt = 0;
-    for (int e = 0; e < E; ++e) {
-      const int j = e * 64 + lane;
-      const bool ge = j < T && score_key(srow[j]) >= cand;
-      cnt += __popcll(__ballot(ge));
+#pragma unroll
+    for (int e = 0; e < (CACHED ? SEL_MAXE : 1); ++e) {
+      if constexpr (CACHED) {
+        if (e < E) cnt += __popcll(__ballot(rk.get(e) >= cand));
+      } else {
+        for (int x = 0; x < E; ++x) cnt += __popcll(__ballot(rk.get(x) >= cand));
+      }
     }
     if (cnt >= kb) th = cand;
   }
-  int gt = 0;
-  for (int e = 0; e < E; ++e) {
-    const int j = e * 64 + lane;
-    gt += __popcll(__ballot(j < T && score_key(srow[j]) > th));
-  }
-  int need = kb - gt;  // ties at th still to take, lowest index first
+  int need = kb;  // ties at th still to take, lowest index first
   int pos = 0;
-  for (int e = 0; e < E; ++e) {
+  auto emit = [&](int e, uint32_t key) {
     const int j = e * 64 + lane;
-    const uint32_t key = j < T ? score_key(srow[j]) : 0u;
-    const uint64_t bgt = __ballot(j < T && key > th);
-    uint64_t beq = __ballot(j < T && key == th);
+    const uint64_t bgt = __ballot(key > th);
+    uint64_t beq = __ballot(key == th);
     uint64_t take = 0ull;
     if (need > 0) {
       if (__popcll(beq) <= need) {
@@ -71,10 +93,42 @@ __device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, int
       need -= __popcll(take);
     }
     const uint64_t sel = bgt | take;
-    if (lane == 0) mrow[e] = sel;
+    if (lane == 0) {
+      mrow[e] = sel;
+      if (mcol) mcol[(size_t)e * T] = sel;
+    }
     if ((sel >> lane) & 1ull) krow[pos + __popcll(sel & ((1ull << lane) - 1ull))] = j;
     pos += __popcll(sel);
+  };
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int e = 0; e < SEL_MAXE; ++e)
+      if (e < E) need -= __popcll(__ballot(rk.get(e) > th));
+#pragma unroll
+    for (int e = 0; e < SEL_MAXE; ++e)
+      if (e < E) emit(e, rk.get(e));
+  } else {
+    for (int e = 0; e < E; ++e) need -= __popcll(__ballot(rk.get(e) > th));
+    for (int e = 0; e < E; ++e) emit(e, rk.get(e));
   }
+  (void)EMAX;
+}
+
+// mrow: the row's W64 words; mcol (may be null): word e goes to mcol[e * T]
+__device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, uint64_t *mcol,
+                           int32_t *krow, int lane) {
+  const int E = (T + 63) >> 6;
+  if (kb <= 0) {
+    for (int e = lane; e < E; e += 64) {
+      mrow[e] = 0ull;
+      if (mcol) mcol[(size_t)e * T] = 0ull;
+    }
+    return;
+  }
+  if (E <= SEL_MAXE)
+    select_row_t<true>(srow, T, kb, mrow, mcol, krow, lane);
+  else
+    select_row_t<false>(srow, T, kb, mrow, mcol, krow, lane);
 }
 
 template <int D>
@@ -83,6 +137,7 @@ __global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ q
                                                      const float *__restrict__ mu, int T, int R,
                                                      int kb, int W64,
                                                      uint64_t *__restrict__ mask,
+                                                     uint64_t *__restrict__ maskt,
                                                      int32_t *__restrict__ kept) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float *sq = smem;          // [R][D]
@@ -127,7 +182,9 @@ __global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ q
   const int w = tid >> 6, lane = tid & 63;
   for (int r = w; r < nr; r += 4) {
     const size_t row = (size_t)bh * T + i0 + r;
-    select_row(ss + r * T, T, kb, mask + row * W64, kept + row * (size_t)(kb > 0 ? kb : 1), lane);
+    uint64_t *mcol = maskt ? maskt + (size_t)bh * W64 * T + i0 + r : nullptr;
+    select_row(ss + r * T, T, kb, mask + row * W64, mcol, kept + row * (size_t)(kb > 0 ? kb : 1),
+               lane);
   }
 }
 
@@ -138,10 +195,10 @@ void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   dim3 grid(p.BH * groups), block(256);
   if (p.d == 128)
     hipLaunchKernelGGL(k_scores_topk<128>, grid, block, lds, st, ws.qbar, ws.kbar, ws.mu, p.T, R,
-                       p.kb, p.W64, ws.mask, ws.kept);
+                       p.kb, p.W64, ws.mask, p.lin_on ? ws.maskt : nullptr, ws.kept);
   else
     hipLaunchKernelGGL(k_scores_topk<64>, grid, block, lds, st, ws.qbar, ws.kbar, ws.mu, p.T, R,
-                       p.kb, p.W64, ws.mask, ws.kept);
+                       p.kb, p.W64, ws.mask, p.lin_on ? ws.maskt : nullptr, ws.kept);
 }
 
 }  // namespace sla

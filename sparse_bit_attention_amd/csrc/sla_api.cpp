@@ -31,6 +31,7 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.dk = (float *)(b + p.off[R_DK]);
   w.dkn = (float *)(b + p.off[R_DKN]);
   w.flags = (int32_t *)(b + p.off[R_FLAG]);
+  w.maskt = (uint64_t *)(b + p.off[R_MASKT]);
   w.vt = (uint16_t *)(b + p.off[R_VT]);
   w.qb = (uint16_t *)(b + p.off[R_QB]);
   w.kbf = (uint16_t *)(b + p.off[R_KB]);
@@ -125,6 +126,7 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_DK] = bt * 4;
   p.size[R_DKN] = bt * 4;
   p.size[R_FLAG] = bt * 4;
+  p.size[R_MASKT] = p.lin_on ? bt * p.W64 * 8 : 0;
   p.size[R_VT] = blk_elems * 2;
   p.size[R_QB] = p.qk_int8 ? 0 : blk_elems * 2;
   p.size[R_KB] = p.qk_int8 ? 0 : blk_elems * 2;

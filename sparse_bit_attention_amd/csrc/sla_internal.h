@@ -23,6 +23,7 @@ enum Region {
   R_DK = SLA_WS_DK,
   R_DKN,  // f32 dk_j * max row L2 norm of the block's K8 codes   [BH][T]
   R_FLAG, // i32 query blocks left to the online-max attention    [BH][T]
+  R_MASKT,// u64 mask words, word-major                          [BH][W64][T]
   R_VT,   // bf16 V per key block in kmaj_off order              [BH][T][64*d]
   R_QB,   // bf16 Q per query block, fragment order (bf16 QK^T)  [BH][T][64*d]
   R_KB,   // bf16 K per key block, fragment order (bf16 QK^T)    [BH][T][64*d]
@@ -45,7 +46,7 @@ struct Plan {
 
 struct WsPtrs {
   float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn;
-  uint64_t *mask;
+  uint64_t *mask, *maskt;
   int32_t *kept, *flags;
   int8_t *q8, *k8;
   uint16_t *vt, *qb, *kbf, *wsw, *hb, *hi;
