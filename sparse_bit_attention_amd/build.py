@@ -34,9 +34,15 @@ FLAGS = [
 ]
 
 
+# Per-file extra flags.  The attention kernel keeps its MFMA results in VGPRs:
+# its softmax reads the QK^T accumulators with vector ALU code, and the AGPR
+# form would add an AGPR -> VGPR copy per score.
+EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[-4:-4] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

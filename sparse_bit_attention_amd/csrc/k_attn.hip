@@ -74,18 +74,38 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
 // Copy nfrag 1 KiB fragments global -> LDS; lane l moves bytes [16l, 16l+16)
-// of each fragment, which land at the same offsets in LDS.
-__device__ __forceinline__ void dma_frags(const uint4 *src, uint4 *dst, int nfrag, int lane) {
-  for (int f = 0; f < nfrag; ++f)
-    __builtin_amdgcn_global_load_lds((gbl_void *)(src + f * 64 + lane), (lds_void *)(dst + f * 64), 16,
-                                     0, 0);
+// of each fragment, which land at the same offsets in LDS.  Four fragments
+// share one address: the instruction's immediate offset advances the global
+// and the LDS address together.
+template <int NFRAG>
+__device__ __forceinline__ void dma_frags(const uint4 *src, uint4 *dst, int lane) {
+  static_assert(NFRAG % 4 == 0, "fragments come in groups of four");
+#pragma unroll
+  for (int f0 = 0; f0 < NFRAG; f0 += 4) {
+    gbl_void *gp = (gbl_void *)(src + f0 * 64 + lane);
+    lds_void *lp = (lds_void *)(dst + f0 * 64);
+    __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gp, lp, 16, 1024, 0);
+    __builtin_amdgcn_global_load_lds(gp, lp, 16, 2048, 0);
+    __builtin_amdgcn_global_load_lds(gp, lp, 16, 3072, 0);
+  }
 }
+
+// The QK^T accumulators of the bound path start at the bit pattern of
+// 1.5 * 2^23: with |score| < 2^22 the int32 sum then reads as the float
+// 12582912 + score, so no int -> float conversion is needed; the constant is
+// folded into the FMA.  Rounding that folded constant shifts a key block's
+// logits by at most 0.75 c (log2 units), so this path is only taken when
+// c <= 2^-10 for every kept block of the row.
+constexpr int SCORE_BIAS_BITS = 0x4B400000;
+constexpr float SCORE_BIAS = 12582912.0f;
+constexpr float BIAS_C_LIMIT = 0x1p-10f;
 
 // Probabilities of one 32-key half for query tile U as a bf16 B fragment (k
 // order of kmaj_off) and their sum: p = exp2(score * c - m).
-template <int U>
+template <int U, bool BIASED>
 __device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m, float &lsum) {
-  const float nm = -m;
+  const float nm = BIASED ? -__builtin_fmaf(SCORE_BIAS, c, m) : -m;
   const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
   // The pairs stay in scalars: bit-casting an element of an ext-vector is
   // miscompiled by this clang (every element reads element 0).
@@ -93,8 +113,11 @@ __device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const int e0 = 2 * h, e1 = 2 * h + 1;
-    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[e0 >> 2][U][e0 & 3], c, nm));
-    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[e1 >> 2][U][e1 & 3], c, nm));
+    const int a0 = s[e0 >> 2][U][e0 & 3], a1 = s[e1 >> 2][U][e1 & 3];
+    const float f0 = BIASED ? __int_as_float(a0) : (float)a0;
+    const float f1 = BIASED ? __int_as_float(a1) : (float)a1;
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(f0, c, nm));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(f1, c, nm));
     pk[h] = pack2bf(x0, x1);
     lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[h]), one, lsum, false);
   }
@@ -116,8 +139,8 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
   constexpr int VFR = 2 * 64 * D / 1024;
   if (kb > 0) {
     const int j0 = kl[0];
-    dma_frags(k8u + (headblk + j0) * KFR * 64, kslot, KFR, lane);
-    dma_frags(vtu + (headblk + j0) * VFR * 64, vslot0, VFR, lane);
+    dma_frags<KFR>(k8u + (headblk + j0) * KFR * 64, kslot, lane);
+    dma_frags<VFR>(vtu + (headblk + j0) * VFR * 64, vslot0, lane);
   }
   for (int n = 0; n < kb; ++n) {
     const int j = kl[n];
@@ -136,8 +159,8 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
     __builtin_amdgcn_sched_barrier(0);
     if (n + 1 < kb) {
       const int jn = kl[n + 1];
-      dma_frags(k8u + (headblk + jn) * KFR * 64, kslot, KFR, lane);
-      dma_frags(vtu + (headblk + jn) * VFR * 64, vslot0 + ((n + 1) & 1) * VFR * 64, VFR, lane);
+      dma_frags<KFR>(k8u + (headblk + jn) * KFR * 64, kslot, lane);
+      dma_frags<VFR>(vtu + (headblk + jn) * VFR * 64, vslot0 + ((n + 1) & 1) * VFR * 64, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -148,7 +171,8 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          v4i acc = {0, 0, 0, 0};
+          const int init = BOUND ? SCORE_BIAS_BITS : 0;
+          v4i acc = {init, init, init, init};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(kf[2 * hf + t2][kc], qf[u][kc], acc);
           s[t2][u] = acc;
@@ -182,10 +206,10 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
         }
       }
       v4u pf[4];
-      pf[0] = probs_half<0>(s, c, m[0], lsum[0]);
-      pf[1] = probs_half<1>(s, c, m[1], lsum[1]);
-      pf[2] = probs_half<2>(s, c, m[2], lsum[2]);
-      pf[3] = probs_half<3>(s, c, m[3], lsum[3]);
+      pf[0] = probs_half<0, BOUND>(s, c, m[0], lsum[0]);
+      pf[1] = probs_half<1, BOUND>(s, c, m[1], lsum[1]);
+      pf[2] = probs_half<2, BOUND>(s, c, m[2], lsum[2]);
+      pf[3] = probs_half<3, BOUND>(s, c, m[3], lsum[3]);
       v4u vf[CG];
 #pragma unroll
       for (int a = 0; a < CG; ++a) vf[a] = __builtin_bit_cast(v4u, vcur[(hf * CG + a) * 64 + lane]);
@@ -198,7 +222,10 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
       // padding keys have score 0: remove exactly what the row sums received
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(-m[u]), 0.f);
+        // the same arithmetic the probabilities of a zero score went through
+        const float x = BOUND ? __builtin_fmaf(SCORE_BIAS, c, -__builtin_fmaf(SCORE_BIAS, c, m[u]))
+                              : -m[u];
+        const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(x), 0.f);
         lsum[u] -= (float)npad_lane * bf2f((uint16_t)(pp & 0xFFFF));
       }
     }
@@ -206,8 +233,9 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
 }
 
 // BOUND = true: the main launch.  A query block whose logit bound exceeds
-// BOUND_LIMIT is only flagged (flags[qb] = 1) and left to the second launch,
-// BOUND = false, which runs the online-max loop for flagged blocks only.
+// BOUND_LIMIT, or whose logit scale c exceeds BIAS_C_LIMIT, is only flagged
+// (flags[qb] = 1) and left to the second launch, BOUND = false, which runs the
+// online-max loop (plain int -> float scores) for flagged blocks only.
 template <int D, bool LIN, bool BOUND>
 __global__ __launch_bounds__(256, 1) void k_attn(
     const int8_t *__restrict__ q8, const int8_t *__restrict__ k8, const float *__restrict__ dq,
@@ -251,9 +279,13 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 
   // Upper bound of the row's logits (log2 units): |q8_r . k8_s| <= ||q8_r||
   // ||k8_s||, so logit <= dq_i sm_scale log2(e) ||q8_r|| max_j (dk_j max_s ||k8_s||).
-  float kmax = 0.f;
-  for (int n = 0; n < kb; ++n) kmax = fmaxf(kmax, dkn[headblk + kl[n]]);
-  bool bounded = true;
+  float kmax = 0.f, dkmax = 0.f;
+  for (int n = 0; n < kb; ++n) {
+    const int jj = kl[n];
+    kmax = fmaxf(kmax, dkn[headblk + jj]);
+    dkmax = fmaxf(dkmax, dk[headblk + jj]);
+  }
+  bool bounded = dqi * dkmax <= BIAS_C_LIMIT;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     int sq = 0;
