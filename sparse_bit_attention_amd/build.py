@@ -37,7 +37,7 @@ FLAGS = [
 # Per-file extra flags.  The attention kernel keeps its MFMA results in VGPRs:
 # its softmax reads the QK^T accumulators with vector ALU code, and the AGPR
 # form would add an AGPR -> VGPR copy per score.
-EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {}
 
 
 def _compile(src: str) -> str:

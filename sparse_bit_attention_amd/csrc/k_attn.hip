@@ -65,30 +65,29 @@ __device__ __forceinline__ void qk_int8(const v4i (&kf)[4][D / 64], const v4i (&
     }
 }
 
-// s_waitcnt with only vmcnt = 0 (expcnt, lgkmcnt left at their maxima)
-#define SLA_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
-// s_waitcnt with only lgkmcnt = 0
-#define SLA_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+// One key block's operands, straight from HBM in register layout: the K8
+// fragments (A operands of S^T) and the V^T fragments of both 32-key halves
+// (A operands of O^T).
+template <int D>
+struct KVBlock {
+  v4i k[4][D / 64];
+  v4u v[2][D / 16];
+};
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
-
-// Copy nfrag 1 KiB fragments global -> LDS; lane l moves bytes [16l, 16l+16)
-// of each fragment, which land at the same offsets in LDS.  Four fragments
-// share one address: the instruction's immediate offset advances the global
-// and the LDS address together.
-template <int NFRAG>
-__device__ __forceinline__ void dma_frags(const uint4 *src, uint4 *dst, int lane) {
-  static_assert(NFRAG % 4 == 0, "fragments come in groups of four");
+template <int D>
+__device__ __forceinline__ void load_kv(KVBlock<D> &x, const uint4 *k8u, const uint4 *vtu,
+                                        size_t blk, int lane) {
+  constexpr int KC = D / 64, CG = D / 16;
+  const uint4 *kp = k8u + blk * (4 * KC * 64) + lane;
+  const uint4 *vp = vtu + blk * (2 * CG * 64) + lane;
 #pragma unroll
-  for (int f0 = 0; f0 < NFRAG; f0 += 4) {
-    gbl_void *gp = (gbl_void *)(src + f0 * 64 + lane);
-    lds_void *lp = (lds_void *)(dst + f0 * 64);
-    __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gp, lp, 16, 1024, 0);
-    __builtin_amdgcn_global_load_lds(gp, lp, 16, 2048, 0);
-    __builtin_amdgcn_global_load_lds(gp, lp, 16, 3072, 0);
-  }
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) x.k[t][kc] = __builtin_bit_cast(v4i, kp[(t * KC + kc) * 64]);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int a = 0; a < CG; ++a) x.v[hf][a] = __builtin_bit_cast(v4u, vp[(hf * CG + a) * 64]);
 }
 
 // The QK^T accumulators of the bound path start at the bit pattern of
@@ -124,112 +123,347 @@ __device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m
   return v4u{pk[0], pk[1], pk[2], pk[3]};
 }
 
-// The kept-block loop, each key block in two 32-key halves
-// (QK^T half -> probabilities -> PV half).  BOUND: m is an upper bound of
-// every logit of the row (set before the loop): no running max, no rescaling.
-// Otherwise m is a running max, moved lazily per half.
+// One kept key block, in two 32-key halves (QK^T half -> probabilities -> PV
+// half).  BOUND: m is an upper bound of every logit of the row (set before the
+// loop): no running max, no rescaling.  Otherwise m is a running max, moved
+// lazily per half.
+template <int D, bool BOUND>
+__device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf)[4][D / 64],
+                                             v4f (&o)[D / 16][4], float (&m)[4],
+                                             float (&lsum)[4], float c, bool last,
+                                             int npad_lane) {
+  constexpr int KC = D / 64, CG = D / 16;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    // S^T for key tiles 2hf, 2hf+1
+    v4i s[2][4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int init = BOUND ? SCORE_BIAS_BITS : 0;
+        v4i acc = {init, init, init, init};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(x.k[2 * hf + t2][kc], qf[u][kc], acc);
+        s[t2][u] = acc;
+      }
+    if (!BOUND) {
+      // half-tile max per query (padding keys score 0 and may only raise it)
+      int imax[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int a0 = max(max(s[0][u][0], s[0][u][1]), s[0][u][2]);
+        const int a1 = max(max(s[0][u][3], s[1][u][0]), s[1][u][1]);
+        imax[u] = max(max(a0, a1), max(s[1][u][2], s[1][u][3]));
+      }
+      bool need = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) need |= ((float)imax[u] * c > m[u] + RESCALE_SLACK);
+      if (__ballot(need) != 0ull) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float tm = (float)imax[u] * c;
+          tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+          tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+          if (tm > m[u] + RESCALE_SLACK) {
+            const float alpha = __builtin_amdgcn_exp2f(m[u] - tm);
+            m[u] = tm;
+            lsum[u] *= alpha;
+#pragma unroll
+            for (int a = 0; a < CG; ++a) o[a][u] *= alpha;
+          }
+        }
+      }
+    }
+    v4u pf[4];
+    pf[0] = probs_half<0, BOUND>(s, c, m[0], lsum[0]);
+    pf[1] = probs_half<1, BOUND>(s, c, m[1], lsum[1]);
+    pf[2] = probs_half<2, BOUND>(s, c, m[2], lsum[2]);
+    pf[3] = probs_half<3, BOUND>(s, c, m[3], lsum[3]);
+#pragma unroll
+    for (int a = 0; a < CG; ++a)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[a][u] = mfma_bf16(x.v[hf][a], pf[u], o[a][u]);
+  }
+  if (last && npad_lane > 0) {
+    // padding keys have score 0: remove exactly what the row sums received
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // the same arithmetic the probabilities of a zero score went through
+      const float xz = BOUND ? __builtin_fmaf(SCORE_BIAS, c, -__builtin_fmaf(SCORE_BIAS, c, m[u]))
+                             : -m[u];
+      const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(xz), 0.f);
+      lsum[u] -= (float)npad_lane * bf2f((uint16_t)(pp & 0xFFFF));
+    }
+  }
+}
+
+// The kept-block loop.  Two register sets alternate: the loads of block n+1
+// are issued before block n is computed, so each load has a whole block of
+// work to land, and no operand passes through LDS.
 template <int D, bool BOUND>
 __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D / 16][4],
                                           float (&m)[4], float (&lsum)[4], const int32_t *kl,
                                           int kb, const float *dk, const uint4 *k8u,
                                           const uint4 *vtu, size_t headblk, float dqi, int T,
-                                          int npad_lane, uint4 *kslot, uint4 *vslot0, int lane) {
-  constexpr int KC = D / 64, CG = D / 16;
-  constexpr int KFR = 64 * D / 1024;
-  constexpr int VFR = 2 * 64 * D / 1024;
-  if (kb > 0) {
-    const int j0 = kl[0];
-    dma_frags<KFR>(k8u + (headblk + j0) * KFR * 64, kslot, lane);
-    dma_frags<VFR>(vtu + (headblk + j0) * VFR * 64, vslot0, lane);
+                                          int npad_lane, int lane) {
+  if (kb <= 0) return;
+  KVBlock<D> xa, xb;
+  load_kv<D>(xa, k8u, vtu, headblk + kl[0], lane);
+  int n = 0;
+  for (; n + 1 < kb; n += 2) {
+    const int ja = kl[n], jb = kl[n + 1];
+    // the scheduling fences keep each block's loads ahead of the other
+    // block's arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+    load_kv<D>(xb, k8u, vtu, headblk + jb, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi * dk[headblk + ja], ja == T - 1, npad_lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 2 < kb) load_kv<D>(xa, k8u, vtu, headblk + kl[n + 2], lane);
+    __builtin_amdgcn_sched_barrier(0);
+    attend_block<D, BOUND>(xb, qf, o, m, lsum, dqi * dk[headblk + jb], jb == T - 1, npad_lane);
   }
-  for (int n = 0; n < kb; ++n) {
-    const int j = kl[n];
-    const float c = dqi * dk[headblk + j];
-    const uint4 *vcur = vslot0 + (n & 1) * VFR * 64;
-    // block n's K8 and V are in LDS once every outstanding copy has landed
-    SLA_WAIT_VMCNT0();
-    __builtin_amdgcn_sched_barrier(0);
-    v4i kf[4][KC];
+  if (n < kb) {
+    const int ja = kl[n];
+    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi * dk[headblk + ja], ja == T - 1, npad_lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined loop of the bound path.  The kept blocks are walked as a
+// stream of 16-key tiles (sub-stage sigma = 4 n + t: block n, key tile t).
+// Sub-stage sigma issues three independent pieces of work, which the
+// scheduler interleaves so that vector ALU work runs while the matrix core is
+// busy:
+//   QK(sigma+1): S^T of tile sigma+1                         (int8 MFMA)
+//   SM(sigma):   probabilities of tile sigma, half a B fragment
+//   PV:          O^T += V^T P^T for the 32-key chunk finished two
+//                sub-stages earlier, half of the channel tiles (bf16 MFMA)
+// Operands come straight from HBM in register layout, through two register
+// rings: K tiles KLEAD sub-stages ahead, V quarters (32 keys x D/2 channels)
+// VLEAD sub-stages ahead.  Nothing passes through LDS, and since every
+// in-flight load is an ordinary register load the compiler's wait counts stay
+// exact.  The loop body covers two blocks, which makes every ring index a
+// constant.
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct Pipe {
+  static constexpr int KC = D / 64, CG = D / 16;
+  static constexpr int KT = KC;          // 1 KiB fragments per K tile (16 keys)
+  static constexpr int VQ = CG / 2;      // 1 KiB fragments per V quarter
+  static constexpr int KLEAD = 4;        // K tile sigma + KLEAD is loaded at sub-stage sigma
+  static constexpr int VLEAD = 4;        // V quarter sigma + VLEAD is loaded at sub-stage sigma
+};
+
+// Probabilities of one 16-key tile for one query tile: four scores in, two
+// bf16 pairs out (k order of kmaj_off), p = exp2(score * c + nm) cut to bf16
+// by keeping the upper half of each float32 (one byte permute per pair).  The
+// row sums are taken by the matrix core from the same bf16 values, so the
+// rounding of p enters numerator and denominator alike.
+__device__ __forceinline__ uint2 probs_tile(const v4i &s, float c, float nm) {
+  uint32_t x[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int r = 0; r < 4; ++r)
+    x[r] = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[r]), c, nm)));
+  // bytes 2,3 of the first value, then bytes 2,3 of the second
+  return make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u));
+}
+
+// A fragment of 16 rows of bf16 ones: the rows of ones^T P^T are row sums of P.
+constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
+
+template <int D>
+struct PipeState {
+  static constexpr int KC = D / 64, CG = D / 16, VQ = CG / 2;
+  v4f o[CG][4];
+  v4f lacc[4];        // row sums (every element of lacc[u] holds the same sum)
+  v4i s[2][4];        // S^T of the two most recent tiles (by tile parity)
+  v4u pf[2][4];       // B fragments of the two most recent 32-key chunks
+  v4i kr[8][KC];      // K tiles (by tile index mod 8)
+  v4u vr[8][VQ];      // V quarters (by quarter index mod 8)
+};
+
+// Block-level values of one loop iteration (two blocks)
+struct PipeBlocks {
+  float c[2];         // logit scale of block 2i, 2i+1
+  float nm[2][4];     // -(bias * c + m_u); -inf for a block past the kept list
+};
+
+// Sub-stage R (0..7) of the loop body; sigma = 8 i + R.
+template <int D, int R>
+__device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D / 64],
+                                          const PipeBlocks &pb, const uint4 *kload_src,
+                                          const uint4 *vload_src, int lane) {
+  using P = Pipe<D>;
+  constexpr int KC = P::KC, VQ = P::VQ;
+  // loads: K tile sigma+KLEAD, V quarter sigma+VLEAD, kept together at the
+  // head of the sub-stage
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        kf[t][kc] = __builtin_bit_cast(v4i, kslot[(t * KC + kc) * 64 + lane]);
-    SLA_WAIT_LGKMCNT0();
-    __builtin_amdgcn_sched_barrier(0);
-    if (n + 1 < kb) {
-      const int jn = kl[n + 1];
-      dma_frags<KFR>(k8u + (headblk + jn) * KFR * 64, kslot, lane);
-      dma_frags<VFR>(vtu + (headblk + jn) * VFR * 64, vslot0 + ((n + 1) & 1) * VFR * 64, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  for (int kc = 0; kc < KC; ++kc)
+    st.kr[(R + P::KLEAD) % 8][kc] = __builtin_bit_cast(v4i, kload_src[kc * 64 + lane]);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // S^T for key tiles 2hf, 2hf+1
-      v4i s[2][4];
+  for (int a = 0; a < VQ; ++a)
+    st.vr[(R + P::VLEAD) % 8][a] = __builtin_bit_cast(v4u, vload_src[a * 64 + lane]);
+  __builtin_amdgcn_sched_barrier(0);
+  // QK(sigma+1)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+  for (int u = 0; u < 4; ++u)
+    st.s[(R + 1) & 1][u] = v4i{SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int init = BOUND ? SCORE_BIAS_BITS : 0;
-          v4i acc = {init, init, init, init};
+  for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(kf[2 * hf + t2][kc], qf[u][kc], acc);
-          s[t2][u] = acc;
-        }
-      if (!BOUND) {
-        // half-tile max per query (padding keys score 0 and may only raise it)
-        int imax[4];
+    for (int u = 0; u < 4; ++u)
+      st.s[(R + 1) & 1][u] = mfma_i8(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
+  // SM(sigma): tile parity R & 1 fills half of chunk sigma/2's B fragment
+  {
+    constexpr int blk = R / 4;
+    constexpr int par = (R / 2) & 1;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int a0 = max(max(s[0][u][0], s[0][u][1]), s[0][u][2]);
-          const int a1 = max(max(s[0][u][3], s[1][u][0]), s[1][u][1]);
-          imax[u] = max(max(a0, a1), max(s[1][u][2], s[1][u][3]));
-        }
-        bool need = false;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) need |= ((float)imax[u] * c > m[u] + RESCALE_SLACK);
-        if (__ballot(need) != 0ull) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float tm = (float)imax[u] * c;
-            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-            if (tm > m[u] + RESCALE_SLACK) {
-              const float alpha = __builtin_amdgcn_exp2f(m[u] - tm);
-              m[u] = tm;
-              lsum[u] *= alpha;
-#pragma unroll
-              for (int a = 0; a < CG; ++a) o[a][u] *= alpha;
-            }
-          }
-        }
-      }
-      v4u pf[4];
-      pf[0] = probs_half<0, BOUND>(s, c, m[0], lsum[0]);
-      pf[1] = probs_half<1, BOUND>(s, c, m[1], lsum[1]);
-      pf[2] = probs_half<2, BOUND>(s, c, m[2], lsum[2]);
-      pf[3] = probs_half<3, BOUND>(s, c, m[3], lsum[3]);
-      v4u vf[CG];
-#pragma unroll
-      for (int a = 0; a < CG; ++a) vf[a] = __builtin_bit_cast(v4u, vcur[(hf * CG + a) * 64 + lane]);
-#pragma unroll
-      for (int a = 0; a < CG; ++a)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o[a][u] = mfma_bf16(vf[a], pf[u], o[a][u]);
-    }
-    if (j == T - 1 && npad_lane > 0) {
-      // padding keys have score 0: remove exactly what the row sums received
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        // the same arithmetic the probabilities of a zero score went through
-        const float x = BOUND ? __builtin_fmaf(SCORE_BIAS, c, -__builtin_fmaf(SCORE_BIAS, c, m[u]))
-                              : -m[u];
-        const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(x), 0.f);
-        lsum[u] -= (float)npad_lane * bf2f((uint16_t)(pp & 0xFFFF));
+    for (int u = 0; u < 4; ++u) {
+      const uint2 pp = probs_tile(st.s[R & 1][u], pb.c[blk], pb.nm[blk][u]);
+      if (R & 1) {
+        st.pf[par][u][2] = pp.x;
+        st.pf[par][u][3] = pp.y;
+      } else {
+        st.pf[par][u][0] = pp.x;
+        st.pf[par][u][1] = pp.y;
       }
     }
   }
+  // PV of chunk sigma/2 - 1, channel tiles [VQ (R&1), VQ (R&1) + VQ), V quarter sigma-2
+  {
+    constexpr int par = ((R / 2) + 1) & 1;
+    constexpr int vs = (R + 6) % 8;
+    constexpr int a0 = (R & 1) * VQ;
+#pragma unroll
+    for (int a = 0; a < VQ; ++a)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par][u], st.o[a0 + a][u]);
+    if ((R & 1) == 0) {
+      const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st.lacc[u] = mfma_bf16(ones, st.pf[par][u], st.lacc[u]);
+    }
+  }
+  constexpr int NMFMA = 4 * KC + 4 * VQ + ((R & 1) == 0 ? 4 : 0);
+  constexpr int VALU_PER = (80 + NMFMA - 1) / NMFMA;
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f (&o)[D / 16][4],
+                                                const float (&m)[4], float (&lsum)[4],
+                                                const int32_t *kl, int kb, const float *dk,
+                                                const uint4 *k8u, const uint4 *vtu,
+                                                size_t headblk, float dqi, int T, int npad_blk,
+                                                int lane) {
+  using P = Pipe<D>;
+  constexpr int KC = P::KC, CG = P::CG, VQ = P::VQ, KT = P::KT;
+  constexpr int KFR = 4 * KT, VFR = 4 * VQ;  // fragments per block
+  if (kb <= 0) return;
+  // global source of K tile x and V quarter x (blocks past the list: the last one)
+  auto kblk = [&](int x) { const int n = x >> 2; return kl[n < kb ? n : kb - 1]; };
+  auto ksrc = [&](int x) { return k8u + ((headblk + kblk(x)) * KFR + (x & 3) * KT) * 64; };
+  auto vsrc = [&](int x) { return vtu + ((headblk + kblk(x)) * VFR + (x & 3) * VQ) * 64; };
+
+  PipeState<D> st;
+#pragma unroll
+  for (int a = 0; a < CG; ++a)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st.o[a][u] = o[a][u];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    st.lacc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    st.pf[1][u] = v4u{0u, 0u, 0u, 0u};  // chunk -1: zero probabilities
+  }
+  // prologue: K tiles 0 .. KLEAD-1, V quarters 0 .. VLEAD-1
+#pragma unroll
+  for (int x = 0; x < P::KLEAD; ++x)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) st.kr[x][kc] = __builtin_bit_cast(v4i, ksrc(x)[kc * 64 + lane]);
+#pragma unroll
+  for (int x = 0; x < P::VLEAD; ++x)
+#pragma unroll
+    for (int a = 0; a < VQ; ++a) st.vr[x][a] = __builtin_bit_cast(v4u, vsrc(x)[a * 64 + lane]);
+  // quarters -2, -1 meet zero probabilities: make them finite
+#pragma unroll
+  for (int a = 0; a < VQ; ++a) {
+    st.vr[6][a] = v4u{0u, 0u, 0u, 0u};
+    st.vr[7][a] = v4u{0u, 0u, 0u, 0u};
+  }
+  // QK(0)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v4i acc = {SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(st.kr[0][kc], qf[u][kc], acc);
+    st.s[0][u] = acc;
+  }
+
+  const int iters = (kb + 1) >> 1;
+  for (int it = 0; it < iters; ++it) {
+    PipeBlocks pb;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int n = 2 * it + e;
+      const bool valid = n < kb;
+      const float c = dqi * dk[headblk + kl[valid ? n : kb - 1]];
+      pb.c[e] = c;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pb.nm[e][u] = valid ? -__builtin_fmaf(SCORE_BIAS, c, m[u]) : -INFINITY;
+    }
+    const int sig = 8 * it;
+#define SLA_SUB(R) \
+    sub_stage<D, R>(st, qf, pb, ksrc(sig + R + P::KLEAD), vsrc(sig + R + P::VLEAD), lane)
+    SLA_SUB(0);
+    SLA_SUB(1);
+    SLA_SUB(2);
+    SLA_SUB(3);
+    SLA_SUB(4);
+    SLA_SUB(5);
+    SLA_SUB(6);
+    SLA_SUB(7);
+#undef SLA_SUB
+  }
+  // drain: PV of the last chunk (parity 1) with V quarters in slots 6 and 7
+  {
+    const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st.lacc[u] = mfma_bf16(ones, st.pf[1][u], st.lacc[u]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int a = 0; a < VQ; ++a)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        st.o[h * VQ + a][u] = mfma_bf16(st.vr[6 + h][a], st.pf[1][u], st.o[h * VQ + a][u]);
+  // complete row sums (every key of every kept block)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) lsum[u] = st.lacc[u][0];
+  // padding keys (score 0) of the last key block: remove their share of the
+  // row sums; a kept list is ascending, so only its last entry can be T-1
+  if (kl[kb - 1] == T - 1 && npad_blk > 0) {
+    const float c = dqi * dk[headblk + T - 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float nm = -__builtin_fmaf(SCORE_BIAS, c, m[u]);
+      const uint32_t x0 = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(SCORE_BIAS, c, nm)));
+      lsum[u] -= (float)npad_blk * __uint_as_float(x0 & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < CG; ++a)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[a][u] = st.o[a][u];
 }
 
 // BOUND = true: the main launch.  A query block whose logit bound exceeds
@@ -244,10 +478,6 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
     int32_t *__restrict__ flags, int N, int T, int kb, int nqb, int F, float qk_scale) {
   constexpr int KC = D / 64, CG = D / 16, KC32 = D / 32;
-  constexpr int KFR = 64 * D / 1024;      // 1 KiB fragments per K8 block
-  constexpr int VFR = 2 * 64 * D / 1024;  // 1 KiB fragments per V block
-  constexpr int SLOT = (KFR + 2 * VFR) * 64;  // uint4 per wave
-  __shared__ uint4 ring[4][SLOT];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
@@ -306,19 +536,17 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     lsum[u] = 0.f;
     bounded = bounded && (m[u] <= BOUND_LIMIT);
   }
-  uint4 *kslot = ring[w];
-  uint4 *vslot0 = ring[w] + KFR * 64;
   if (BOUND) {
     const bool fail = __ballot(!bounded) != 0ull;
     if (lane == 0) flags[qb] = fail ? 1 : 0;
     if (fail) return;
-    kept_loop<D, true>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
-                       dqi, T, npad_lane, kslot, vslot0, lane);
+    kept_loop_piped<D>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
+                       dqi, T, BLK - nlast, lane);
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) m[u] = -INFINITY;
     kept_loop<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
-                        dqi, T, npad_lane, kslot, vslot0, lane);
+                        dqi, T, npad_lane, lane);
   }
   // Row sums; O is normalised only while it is stored, so the accumulators
   // are not touched by vector ALU code in between (they stay in AGPRs).
@@ -326,8 +554,10 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float l = lsum[u];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    if (!BOUND) {  // the online loop keeps per-lane partial sums
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+    }
     // no kept key (kb = 0): O is zero, and l = 1 leaves the linear branch as is
     lrow[u] = l > 0.f ? l : 1.0f;
     linv[u] = 1.0f / lrow[u];
