@@ -168,155 +168,198 @@ __global__ void k_w_swizzle(const uint16_t *__restrict__ W, int D, uint16_t *__r
   }
 }
 
-// H[i][f] = sum_j (1 - M[i][j]) Hb[j][f] for one head and a 32-column slice
-// of f, all query-block rows i at once (so each Hb element is read once per
-// head).  8 waves; wave w owns row tiles [MW*w, MW*w + MW) (16 rows each).
-// Per step of 64 key blocks j: the B slice (64 x 32 bf16) is staged in LDS
-// transposed to [f][j] so a lane's 8 consecutive j are one 16-byte read; the A
-// fragments come from the row's mask word through a 16-entry LDS table that
-// expands 4 complemented mask bits to 4 bf16 ones/zeros (8 bytes per entry:
-// the 16 entries sit in distinct banks, so lookups never conflict).
-constexpr int MARG_TN = 32;   // columns per workgroup
-constexpr int MARG_TK = 64;   // key blocks per step (one mask word)
-constexpr int MARG_MW = 10;   // row tiles per wave: 8 * 10 * 16 = 1280 rows per pass
+// H[i][f] = sum_j (1 - M[i][j]) Hb[j][f]: per head a [T x T] by [T x F] GEMM,
+// 32x32x16 bf16 MFMA with float32 accumulation, written back as bf16.
+// A workgroup (4 waves, 2 x 2) owns a 256 x 256 output tile; each wave a
+// 128 x 128 sub-tile held in 16 accumulator tiles.  Per step of 32 key blocks
+// both operand tiles are built in LDS in MFMA fragment order (1 KiB per
+// fragment, 16 bytes per lane): A from the rows' mask words (the complement
+// bits become bf16 ones and zeros by integer arithmetic), B from Hb rows
+// transposed to key pairs per column.  Two LDS buffers: step s+1 is built
+// while step s is multiplied.  The row tiles of one column tile run one after
+// another on one XCD, so each Hb column slice comes from HBM once.
+constexpr int MG_BM = 256;  // rows per workgroup
+constexpr int MG_BN = 256;  // columns per workgroup
+constexpr int MG_BK = 32;   // key blocks per step
 
 template <int D>
-__global__ __launch_bounds__(512) void k_marginal(const uint64_t *__restrict__ maskt,
-                                                  const uint16_t *__restrict__ hb, int T, int W64,
-                                                  int F, uint16_t *__restrict__ hi) {
-  constexpr int PB = MARG_TK + 8;  // bf16 pitch of the transposed B slice (16-byte rows)
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][MARG_TN * PB];
-  __shared__ __attribute__((aligned(16))) uint2 lut[16];
-  const int nslices = F / MARG_TN;
-  const int mpasses = (T + 8 * MARG_MW * 16 - 1) / (8 * MARG_MW * 16);
-  // consecutive column slices of a head share 128-byte Hb lines: keep them
-  // on one XCD
+__global__ __launch_bounds__(256, 1) void k_marginal(const uint64_t *__restrict__ maskt,
+                                                     const uint16_t *__restrict__ hb, int T,
+                                                     int W64, int F, uint16_t *__restrict__ hi) {
+  // two operand buffers of 32 KiB (A fragments, then B fragments); the
+  // epilogue reuses all 128 KiB to stage each wave's bf16 tile
+  __shared__ __attribute__((aligned(16))) uint4 smem[8192];
+  const int RT = (T + MG_BM - 1) / MG_BM, CT = (F + MG_BN - 1) / MG_BN;
   int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int ns = b % nslices;
-  b /= nslices;
-  const int mp = b % mpasses;
-  const int bh = b / mpasses;
+  const int rt = b % RT;
+  b /= RT;
+  const int ct = b % CT;
+  const int bh = b / CT;
+  const int row0 = rt * MG_BM, col0 = ct * MG_BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, l16 = lane & 15;
-  const int f_base = ns * MARG_TN;
-  const int row0 = mp * (8 * MARG_MW * 16) + w * (MARG_MW * 16);
-  const uint16_t *hbh = hb + (size_t)bh * T * F + f_base;
+  const int wr = w >> 1, wc = w & 1;
+  const uint16_t *hbh = hb + (size_t)bh * T * F;
   const uint64_t *mh = maskt + (size_t)bh * W64 * T;  // word-major: [W64][T]
 
-  if (tid < 16) {
-    uint32_t v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      v[h] = (((tid >> (2 * h)) & 1) ? 0x3F80u : 0u) | (((tid >> (2 * h + 1)) & 1) ? 0x3F800000u : 0u);
-    lut[tid] = make_uint2(v[0], v[1]);
-  }
-
-  v4f acc[MARG_MW][2];
-#pragma unroll
-  for (int a = 0; a < MARG_MW; ++a) {
-    acc[a][0] = v4f{0.f, 0.f, 0.f, 0.f};
-    acc[a][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // one B step: 64 rows j x 32 columns; thread t loads 4 columns of row t/8
-  const int bj = tid >> 3, bf4 = (tid & 7) * 4;
-  auto load_b = [&](int j0) -> uint2 {
-    const int j = j0 + bj;
-    uint2 v = make_uint2(0u, 0u);
-    if (j < T) v = *(const uint2 *)(hbh + (size_t)j * F + bf4);
-    return v;
+  // A: thread tid builds row row0 + tid (32 keys = 4 chunks of 8) from its
+  // mask word, which is loaded two steps ahead
+  const int arow = row0 + tid;
+  // rows past T read row T-1 (their outputs are never stored)
+  const int arow_c = min(arow, T - 1);
+  auto load_word = [&](int s) -> uint64_t {
+    const int word = min((s * MG_BK) >> 6, W64 - 1);
+    return mh[(size_t)word * T + arow_c];
   };
-  auto store_b = [&](int buf, uint2 v) {
-    uint16_t *d = &sB[buf][bf4 * PB + bj];
-    d[0] = (uint16_t)(v.x & 0xFFFF);
-    d[PB] = (uint16_t)(v.x >> 16);
-    d[2 * PB] = (uint16_t)(v.y & 0xFFFF);
-    d[3 * PB] = (uint16_t)(v.y >> 16);
-  };
-
-  // mask words of this lane's rows, fetched one step ahead
-  auto load_words = [&](int st, uint64_t (&wd)[MARG_MW]) {
+  auto gen_a = [&](int s, uint64_t wd, uint4 *buf) {
+    const int j0 = s * MG_BK;
+    uint32_t nb = ~(uint32_t)(wd >> (j0 & 32));
+    const int nvalid = T - j0;  // key blocks past T contribute nothing
+    if (nvalid < 32) nb &= nvalid > 0 ? (1u << nvalid) - 1u : 0u;
 #pragma unroll
-    for (int a = 0; a < MARG_MW; ++a) {
-      const int i = row0 + 16 * a + l16;
-      wd[a] = mh[(size_t)st * T + min(i, T - 1)];
+    for (int c = 0; c < 4; ++c) {
+      // the 8 bits of keys 8c .. 8c+7: even keys to bits 0,2,4,6, odd keys to
+      // bits 16,18,20,22; then bit pair h times (1.0bf16 >> 2h) is the dword
+      // holding keys 2h (low half) and 2h+1 (high half)
+      const uint32_t by = (nb >> (8 * c)) & 0xFFu;
+      const uint32_t y = (by & 0x55u) | (((by >> 1) & 0x55u) << 16);
+      uint4 v;
+      v.x = __umul24(y & 0x00010001u, 0x3F80u);
+      v.y = __umul24(y & 0x00040004u, 0x3F80u >> 2);
+      v.z = __umul24(y & 0x00100010u, 0x3F80u >> 4);
+      v.w = __umul24(y & 0x00400040u, 0x3F80u >> 6);
+      // fragment (row tile tid/32, k-substep c/2), lane (row%32) + 32 (c%2)
+      buf[((tid >> 5) * 2 + (c >> 1)) * 64 + (tid & 31) + 32 * (c & 1)] = v;
     }
   };
-  // rows past T read a valid row and are then forced to "all kept" (A = 0)
-  uint64_t rowpad[MARG_MW];
+  // B: thread tid stages keys 2p, 2p+1 (p = tid/16) x columns 16q .. 16q+15
+  // (q = tid%16) of the tile
+  const int bp = tid >> 4, bq = tid & 15;
+  // key blocks past T read row T-1 (their A entries are 0) and columns past F
+  // read the last 8 columns (their outputs are never stored): no branches
+  const int bcol0 = min(col0 + 16 * bq, F - 16);
+  auto load_b = [&](int s, uint4 (&v)[2][2]) {
+    const int j0 = s * MG_BK;
 #pragma unroll
-  for (int a = 0; a < MARG_MW; ++a) rowpad[a] = (row0 + 16 * a + l16) < T ? 0ull : ~0ull;
-  const int steps = (T + MARG_TK - 1) / MARG_TK;
-  uint64_t wnext[MARG_MW];
-  load_words(0, wnext);
-  uint2 rb = load_b(0);
-  store_b(0, rb);
+    for (int e = 0; e < 2; ++e) {
+      const int j = min(j0 + 2 * bp + e, T - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v[e][h] = *(const uint4 *)(hbh + (size_t)j * F + bcol0 + 8 * h);
+    }
+  };
+  // B fragment layout in LDS: column cl (tile-relative) and key pair p go to
+  // fragment (cl/32, p/8), 16-byte slot ((cl%32) + 32 ((p/4)%2)) ^ ((cl/16)%8),
+  // dword p%4.  The XOR spreads one transposing store over all banks (lanes
+  // differ in cl/16 and p%4) and keeps each 8-lane group of a fragment read on
+  // distinct slots.  Thread (p, q) writes columns 16q + j, j < 16.
+  const int xw = bq & 7;
+  const int bbase = (((bq >> 1) * 2 + (bp >> 3)) * 64 + 16 * (bq & 1) + 32 * ((bp >> 2) & 1)) * 4 + (bp & 3);
+  int boff[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) boff[jj] = bbase + 4 * (jj ^ xw);
+  auto store_b = [&](const uint4 (&v)[2][2], uint4 *buf) {
+    uint32_t *bw = (uint32_t *)(buf + 1024);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d0[4] = {v[0][h].x, v[0][h].y, v[0][h].z, v[0][h].w};
+      const uint32_t d1[4] = {v[1][h].x, v[1][h].y, v[1][h].z, v[1][h].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // column 2m: both keys' low halves; column 2m+1: both high halves
+        bw[boff[2 * m] + 32 * h] = __builtin_amdgcn_perm(d1[m], d0[m], 0x05040100u);
+        bw[boff[2 * m + 1] + 32 * h] = __builtin_amdgcn_perm(d1[m], d0[m], 0x07060302u);
+      }
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  // Step s multiplies buffer s&1 and builds step s+1 into the other buffer
+  // from registers loaded during step s-1; its own loads are for step s+2.
+  // The loop runs two steps per iteration so the two register sets keep
+  // fixed names (a copy would wait for the loads in flight).
+  // an even number of steps (a step past T has an all-zero A)
+  const int steps = (((T + MG_BK - 1) / MG_BK) + 1) & ~1;
+  uint4 bvA[2][2], bvB[2][2];
+  uint64_t wdA, wdB;
+  {
+    uint4 b0[2][2];
+    load_b(0, b0);
+    const uint64_t w0 = load_word(0);
+    load_b(1, bvA);
+    wdA = load_word(1);
+    gen_a(0, w0, smem);
+    store_b(b0, smem);
+  }
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    const int j0 = s * MARG_TK;
-    uint64_t wcur[MARG_MW];
+  auto mma_step = [&](const uint4 *cur) {
 #pragma unroll
-    for (int a = 0; a < MARG_MW; ++a) wcur[a] = wnext[a];
-    if (s + 1 < steps) {
-      rb = load_b(j0 + MARG_TK);
-      load_words(s + 1, wnext);
+    for (int ks = 0; ks < 2; ++ks) {
+      v4u af[4], bf[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) af[x] = __builtin_bit_cast(v4u, cur[((4 * wr + x) * 2 + ks) * 64 + lane]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int ctile = 4 * wc + y;
+        const int slot = lane ^ ((2 * ctile + ((lane & 31) >> 4)) & 7);
+        bf[y] = __builtin_bit_cast(v4u, cur[1024 + (ctile * 2 + ks) * 64 + slot]);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = mfma32_bf16(af[x], bf[y], acc[x][y]);
     }
-    // key blocks j0 + 32kc + 8g + e past T must give A = 0: set their mask
-    // bits (kept) before complementing; only the last step is short
-    uint32_t pad[2] = {0u, 0u};
-    if (j0 + MARG_TK > T) {
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int n = T - (j0 + 32 * kc);
-        pad[kc] = n >= 32 ? 0u : (n <= 0 ? ~0u : (~0u << n));
-      }
-    }
-    v4u bfr[2][2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        bfr[nt][kc] = *(const v4u *)(&sB[buf][(16 * nt + l16) * PB + 32 * kc + 8 * g]);
-    // all A fragments of the step first (one LDS wait), then the products
-    v4u af[MARG_MW][2];
-#pragma unroll
-    for (int a = 0; a < MARG_MW; ++a)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const uint32_t half = (uint32_t)((wcur[a] | rowpad[a]) >> (32 * kc)) | pad[kc];
-        const uint32_t nb = ~half;
-        const uint2 lo = lut[__builtin_amdgcn_ubfe(nb, 8 * g, 4)];
-        const uint2 hi4 = lut[__builtin_amdgcn_ubfe(nb, 8 * g + 4, 4)];
-        af[a][kc] = v4u{lo.x, lo.y, hi4.x, hi4.y};
-      }
-#pragma unroll
-    for (int a = 0; a < MARG_MW; ++a)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        acc[a][0] = mfma_bf16(af[a][kc], bfr[0][kc], acc[a][0]);
-        acc[a][1] = mfma_bf16(af[a][kc], bfr[1][kc], acc[a][1]);
-      }
-    // issue order: index math, every LDS read, then the products
-    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * MARG_MW + 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MARG_MW, 0);
-    if (s + 1 < steps) store_b(buf ^ 1, rb);
+  };
+  for (int s = 0; s < steps; s += 2) {
+    // even step s: buffer 0; builds s+1 (bvA, wdA) into buffer 1; loads s+2
+    load_b(s + 2, bvB);
+    wdB = load_word(s + 2);
+    mma_step(smem);
+    gen_a(s + 1, wdA, smem + 2048);
+    store_b(bvA, smem + 2048);
+    __syncthreads();
+    // odd step s+1: buffer 1; builds s+2 (bvB, wdB) into buffer 0; loads s+3
+    load_b(s + 3, bvA);
+    wdA = load_word(s + 3);
+    mma_step(smem + 2048);
+    gen_a(s + 2, wdB, smem);
+    store_b(bvB, smem);
     __syncthreads();
   }
-  // store bf16 rows i < T: lane holds column 16nt + l16, rows 4g + r of each tile
-  uint16_t *hih = hi + (size_t)bh * T * F + f_base;
+
+  // epilogue: each wave stages its 128 x 128 tile as bf16 rows (256 B pitch),
+  // then writes 16-byte pieces of rows < T, columns < F
+  uint16_t *st = (uint16_t *)(smem + w * 2048);
 #pragma unroll
-  for (int a = 0; a < MARG_MW; ++a)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = row0 + 16 * a + 4 * g + r;
-      if (i < T) {
-        hih[(size_t)i * F + l16] = f2bf(acc[a][0][r]);
-        hih[(size_t)i * F + 16 + l16] = f2bf(acc[a][1][r]);
+    for (int y = 0; y < 4; ++y) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * x + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int cc = 32 * y + (lane & 31);
+        st[rr * 128 + cc] = f2bf(acc[x][y][r]);
       }
+      // one accumulator tile at a time (keeps the register demand small)
+      __builtin_amdgcn_sched_barrier(0);
     }
+  __syncthreads();
+  const int orow0 = row0 + 128 * wr, ocol0 = col0 + 128 * wc;
+  uint16_t *hih = hi + (size_t)bh * T * F;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int piece = it * 64 + lane;  // 16 pieces of 8 columns per row
+    const int rr = piece >> 4, c8 = (piece & 15) * 8;
+    const int row = orow0 + rr, col = ocol0 + c8;
+    if (row < T && col < F)
+      *(uint4 *)(hih + (size_t)row * F + col) = *(const uint4 *)(st + rr * 128 + c8);
+  }
 }
 
 void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const WsPtrs &ws,
@@ -340,9 +383,8 @@ void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStr
 }
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
-  const int nslices = p.F / MARG_TN;
-  const int mpasses = (p.T + 8 * MARG_MW * 16 - 1) / (8 * MARG_MW * 16);
-  dim3 grid(p.BH * mpasses * nslices), block(512);
+  const int RT = (p.T + MG_BM - 1) / MG_BM, CT = (p.F + MG_BN - 1) / MG_BN;
+  dim3 grid(p.BH * CT * RT), block(256);
   if (p.d == 128)
     hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
   else

@@ -23,6 +23,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -46,6 +47,13 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 
 __device__ __forceinline__ v4f mfma_bf16(v4u a, v4u b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// 32x32x16 bf16: lane l holds A[l%32][8(l/32) .. +7] and B[8(l/32) .. +7][l%32];
+// accumulator register r of lane l is D[8(r/4) + 4(l/32) + r%4][l%32].
+__device__ __forceinline__ v16f mfma32_bf16(v4u a, v4u b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
