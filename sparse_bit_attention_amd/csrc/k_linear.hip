@@ -170,24 +170,40 @@ __global__ void k_w_swizzle(const uint16_t *__restrict__ W, int D, uint16_t *__r
 
 // H[i][f] = sum_j (1 - M[i][j]) Hb[j][f]: per head a [T x T] by [T x F] GEMM,
 // 32x32x16 bf16 MFMA with float32 accumulation, written back as bf16.
-// A workgroup (4 waves, 2 x 2) owns a 256 x 256 output tile; each wave a
-// 128 x 128 sub-tile held in 16 accumulator tiles.  Per step of 32 key blocks
-// both operand tiles are built in LDS in MFMA fragment order (1 KiB per
-// fragment, 16 bytes per lane): A from the rows' mask words (the complement
-// bits become bf16 ones and zeros by integer arithmetic), B from Hb rows
-// transposed to key pairs per column.  Two LDS buffers: step s+1 is built
-// while step s is multiplied.  The row tiles of one column tile run one after
-// another on one XCD, so each Hb column slice comes from HBM once.
+// A workgroup (8 waves, two per SIMD, so one wave's products cover the
+// other's waits) owns a 256 x 256 output tile; wave w owns rows 64 (w/2) ..
+// +63 and columns 128 (w%2) .. +127 in 8 accumulator tiles.  Per step of 32
+// key blocks:
+//  * A (the complement mask as bf16 ones and zeros) is built by each wave in
+//    registers, straight from its rows' mask words;
+//  * B (32 Hb rows x 256 columns) is staged in LDS in MFMA fragment order:
+//    thread (w, l) loads keys 4w .. 4w+3 of columns 4l .. 4l+3 and writes
+//    half of each of those columns' 16-byte fragment slots.  Slots are
+//    XOR-swizzled by their 8-slot group, so both the writes and the fragment
+//    reads spread over all banks.
+// Global loads run two steps ahead; B is double-buffered in LDS.  The row
+// tiles of one column tile run one after another on one XCD, so each Hb
+// column slice comes from HBM once.
 constexpr int MG_BM = 256;  // rows per workgroup
 constexpr int MG_BN = 256;  // columns per workgroup
 constexpr int MG_BK = 32;   // key blocks per step
 
+// 8 mask bits (keys k .. k+7, bit i = key k+i, 1 = use the block) as the four
+// dwords of an MFMA operand: dword h holds key 2h (low half) and 2h+1 (high
+// half) as bf16 1.0 or 0.  Even keys go to bits 0,2,4,6, odd keys to bits
+// 16,18,20,22; bit pair h times (0x3F80 >> 2h) is then dword h.
+__device__ __forceinline__ v4u bits_to_bf16x8(uint32_t by) {
+  const uint32_t y = (by & 0x55u) | (((by >> 1) & 0x55u) << 16);
+  return v4u{(uint32_t)__umul24(y & 0x00010001u, 0x3F80u), (uint32_t)__umul24(y & 0x00040004u, 0x3F80u >> 2),
+             (uint32_t)__umul24(y & 0x00100010u, 0x3F80u >> 4), (uint32_t)__umul24(y & 0x00400040u, 0x3F80u >> 6)};
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_marginal(const uint64_t *__restrict__ maskt,
+__global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict__ maskt,
                                                      const uint16_t *__restrict__ hb, int T,
                                                      int W64, int F, uint16_t *__restrict__ hi) {
-  // two operand buffers of 32 KiB (A fragments, then B fragments); the
-  // epilogue reuses all 128 KiB to stage each wave's bf16 tile
+  // two B buffers of 16 KiB; the epilogue reuses all 128 KiB to stage each
+  // wave's bf16 tile
   __shared__ __attribute__((aligned(16))) uint4 smem[8192];
   const int RT = (T + MG_BM - 1) / MG_BM, CT = (F + MG_BN - 1) / MG_BN;
   int b = xcd_remap(blockIdx.x, gridDim.x);
@@ -202,142 +218,125 @@ __global__ __launch_bounds__(256, 1) void k_marginal(const uint64_t *__restrict_
   const uint16_t *hbh = hb + (size_t)bh * T * F;
   const uint64_t *mh = maskt + (size_t)bh * W64 * T;  // word-major: [W64][T]
 
-  // A: thread tid builds row row0 + tid (32 keys = 4 chunks of 8) from its
-  // mask word, which is loaded two steps ahead
-  const int arow = row0 + tid;
-  // rows past T read row T-1 (their outputs are never stored)
-  const int arow_c = min(arow, T - 1);
-  auto load_word = [&](int s) -> uint64_t {
-    const int word = min((s * MG_BK) >> 6, W64 - 1);
-    return mh[(size_t)word * T + arow_c];
+  // ---- A: lane l owns rows 64 wr + 32 x + l%32 (x < 2) and keys 8 (l/32) ..
+  // +7 of each 16-key half-step.  Rows past T read row T-1 (their outputs are
+  // never stored).
+  int arow[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) arow[x] = min(row0 + 64 * wr + 32 * x + (lane & 31), T - 1);
+  auto load_words = [&](int word, uint64_t (&wd)[2]) {
+    word = min(word, W64 - 1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) wd[x] = mh[(size_t)word * T + arow[x]];
   };
-  auto gen_a = [&](int s, uint64_t wd, uint4 *buf) {
-    const int j0 = s * MG_BK;
-    uint32_t nb = ~(uint32_t)(wd >> (j0 & 32));
-    const int nvalid = T - j0;  // key blocks past T contribute nothing
-    if (nvalid < 32) nb &= nvalid > 0 ? (1u << nvalid) - 1u : 0u;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // the 8 bits of keys 8c .. 8c+7: even keys to bits 0,2,4,6, odd keys to
-      // bits 16,18,20,22; then bit pair h times (1.0bf16 >> 2h) is the dword
-      // holding keys 2h (low half) and 2h+1 (high half)
-      const uint32_t by = (nb >> (8 * c)) & 0xFFu;
-      const uint32_t y = (by & 0x55u) | (((by >> 1) & 0x55u) << 16);
-      uint4 v;
-      v.x = __umul24(y & 0x00010001u, 0x3F80u);
-      v.y = __umul24(y & 0x00040004u, 0x3F80u >> 2);
-      v.z = __umul24(y & 0x00100010u, 0x3F80u >> 4);
-      v.w = __umul24(y & 0x00400040u, 0x3F80u >> 6);
-      // fragment (row tile tid/32, k-substep c/2), lane (row%32) + 32 (c%2)
-      buf[((tid >> 5) * 2 + (c >> 1)) * 64 + (tid & 31) + 32 * (c & 1)] = v;
-    }
-  };
-  // B: thread tid stages keys 2p, 2p+1 (p = tid/16) x columns 16q .. 16q+15
-  // (q = tid%16) of the tile
-  const int bp = tid >> 4, bq = tid & 15;
-  // key blocks past T read row T-1 (their A entries are 0) and columns past F
-  // read the last 8 columns (their outputs are never stored): no branches
-  const int bcol0 = min(col0 + 16 * bq, F - 16);
-  auto load_b = [&](int s, uint4 (&v)[2][2]) {
-    const int j0 = s * MG_BK;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = min(j0 + 2 * bp + e, T - 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v[e][h] = *(const uint4 *)(hbh + (size_t)j * F + bcol0 + 8 * h);
-    }
-  };
-  // B fragment layout in LDS: column cl (tile-relative) and key pair p go to
-  // fragment (cl/32, p/8), 16-byte slot ((cl%32) + 32 ((p/4)%2)) ^ ((cl/16)%8),
-  // dword p%4.  The XOR spreads one transposing store over all banks (lanes
-  // differ in cl/16 and p%4) and keeps each 8-lane group of a fragment read on
-  // distinct slots.  Thread (p, q) writes columns 16q + j, j < 16.
-  const int xw = bq & 7;
-  const int bbase = (((bq >> 1) * 2 + (bp >> 3)) * 64 + 16 * (bq & 1) + 32 * ((bp >> 2) & 1)) * 4 + (bp & 3);
-  int boff[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) boff[jj] = bbase + 4 * (jj ^ xw);
-  auto store_b = [&](const uint4 (&v)[2][2], uint4 *buf) {
-    uint32_t *bw = (uint32_t *)(buf + 1024);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t d0[4] = {v[0][h].x, v[0][h].y, v[0][h].z, v[0][h].w};
-      const uint32_t d1[4] = {v[1][h].x, v[1][h].y, v[1][h].z, v[1][h].w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // column 2m: both keys' low halves; column 2m+1: both high halves
-        bw[boff[2 * m] + 32 * h] = __builtin_amdgcn_perm(d1[m], d0[m], 0x05040100u);
-        bw[boff[2 * m + 1] + 32 * h] = __builtin_amdgcn_perm(d1[m], d0[m], 0x07060302u);
-      }
-    }
-  };
+  const int kshift = 8 * (lane >> 5);
 
-  v16f acc[4][4];
+  // ---- B: thread (w, l) holds keys 4w .. 4w+3 of columns 4l .. 4l+3.  Keys
+  // past T read row T-1 (their A entries are 0); columns past F read the last
+  // four columns (never stored).
+  const int bcol = min(col0 + 4 * lane, F - 4);
+  auto load_b = [&](int s, uint2 (&v)[4]) {
+    const int j0 = s * MG_BK + 4 * w;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int k = 0; k < 4; ++k) v[k] = *(const uint2 *)(hbh + (size_t)min(j0 + k, T - 1) * F + bcol);
+  };
+  // column 4l + i, key group g = w/2 (8 keys): fragment (l/8, g/2), slot s =
+  // 4 (l%8) + i + 32 (g%2), stored at s ^ ((s/8)%8) = 32 (g%2) + 4 ((l%8) ^
+  // (g%2)) + (i ^ (l%8)/2); this thread fills 8 bytes at offset 8 (w%2)
+  const int g8 = w >> 1;
+  int bslot[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    bslot[i] = (((lane >> 3) * 2 + (g8 >> 1)) * 64) + 32 * (g8 & 1) + 4 * ((lane & 7) ^ (g8 & 1)) +
+               (i ^ ((lane & 7) >> 1));
+  auto store_b = [&](const uint2 (&v)[4], uint4 *buf) {
+    uint2 *half = (uint2 *)buf + (w & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t d[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = (i < 2) ? v[2 * h].x : v[2 * h].y;
+        const uint32_t hi2 = (i < 2) ? v[2 * h + 1].x : v[2 * h + 1].y;
+        d[h] = __builtin_amdgcn_perm(hi2, lo, (i & 1) ? 0x07060302u : 0x05040100u);
+      }
+      half[2 * bslot[i]] = make_uint2(d[0], d[1]);
+    }
+  };
+  // fragment reads: lane l reads slot l ^ ((l/8)%8)
+  const int rslot = lane ^ ((lane >> 3) & 7);
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  // Step s multiplies buffer s&1 and builds step s+1 into the other buffer
-  // from registers loaded during step s-1; its own loads are for step s+2.
-  // The loop runs two steps per iteration so the two register sets keep
-  // fixed names (a copy would wait for the loads in flight).
-  // an even number of steps (a step past T has an all-zero A)
-  const int steps = (((T + MG_BK - 1) / MG_BK) + 1) & ~1;
-  uint4 bvA[2][2], bvB[2][2];
-  uint64_t wdA, wdB;
-  {
-    uint4 b0[2][2];
-    load_b(0, b0);
-    const uint64_t w0 = load_word(0);
-    load_b(1, bvA);
-    wdA = load_word(1);
-    gen_a(0, w0, smem);
-    store_b(b0, smem);
-  }
-  __syncthreads();
-  auto mma_step = [&](const uint4 *cur) {
+  // one step: A from the mask words, B from LDS buffer cur
+  auto mma_step = [&](int s, const uint64_t (&wd)[2], const uint4 *cur) {
+    const int j0 = s * MG_BK;
+    const int nvalid = T - j0;  // key blocks past T contribute nothing
+    const uint32_t valid = nvalid >= 32 ? ~0u : (nvalid > 0 ? (1u << nvalid) - 1u : 0u);
+    uint32_t t[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) t[x] = ((~(uint32_t)(wd[x] >> (j0 & 32))) & valid) >> kshift;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v4u af[4], bf[4];
+      v4u af[2], bf[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) af[x] = __builtin_bit_cast(v4u, cur[((4 * wr + x) * 2 + ks) * 64 + lane]);
+      for (int x = 0; x < 2; ++x) af[x] = bits_to_bf16x8((t[x] >> (16 * ks)) & 0xFFu);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int ctile = 4 * wc + y;
-        const int slot = lane ^ ((2 * ctile + ((lane & 31) >> 4)) & 7);
-        bf[y] = __builtin_bit_cast(v4u, cur[1024 + (ctile * 2 + ks) * 64 + slot]);
-      }
+      for (int y = 0; y < 4; ++y) bf[y] = __builtin_bit_cast(v4u, cur[((4 * wc + y) * 2 + ks) * 64 + rslot]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = mfma32_bf16(af[x], bf[y], acc[x][y]);
     }
   };
+
+  // Steps in pairs (an even count; a step past T has an all-zero A): the two
+  // B register sets and the mask words keep fixed names, loaded two steps
+  // (the words: one pair) ahead.
+  const int steps = (((T + MG_BK - 1) / MG_BK) + 1) & ~1;
+  uint2 bvA[4], bvB[4];
+  uint64_t wdc[2], wdn[2];
+  uint4 *buf0 = smem, *buf1 = smem + 1024;
+  {
+    uint2 b0[4];
+    load_b(0, b0);
+    load_b(1, bvA);
+    load_words(0, wdc);
+    store_b(b0, buf0);
+  }
+  __syncthreads();
   for (int s = 0; s < steps; s += 2) {
-    // even step s: buffer 0; builds s+1 (bvA, wdA) into buffer 1; loads s+2
+    // even step s: B buffer 0, words wdc (steps s, s+1).  The fences keep the
+    // transposing stores (which wait for their loads) after the products.
     load_b(s + 2, bvB);
-    wdB = load_word(s + 2);
-    mma_step(smem);
-    gen_a(s + 1, wdA, smem + 2048);
-    store_b(bvA, smem + 2048);
+    load_words((s + 2) >> 1, wdn);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(s, wdc, buf0);
+    __builtin_amdgcn_sched_barrier(0);
+    store_b(bvA, buf1);
     __syncthreads();
-    // odd step s+1: buffer 1; builds s+2 (bvB, wdB) into buffer 0; loads s+3
+    // odd step s+1: B buffer 1
     load_b(s + 3, bvA);
-    wdA = load_word(s + 3);
-    mma_step(smem + 2048);
-    gen_a(s + 2, wdB, smem);
-    store_b(bvB, smem);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(s + 1, wdc, buf1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_b(bvB, buf0);
     __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x) wdc[x] = wdn[x];
   }
 
-  // epilogue: each wave stages its 128 x 128 tile as bf16 rows (256 B pitch),
+  // epilogue: each wave stages its 64 x 128 tile as bf16 rows (256 B pitch),
   // then writes 16-byte pieces of rows < T, columns < F
-  uint16_t *st = (uint16_t *)(smem + w * 2048);
+  uint16_t *st = (uint16_t *)(smem + w * 1024);
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
 #pragma unroll
@@ -350,10 +349,10 @@ __global__ __launch_bounds__(256, 1) void k_marginal(const uint64_t *__restrict_
       __builtin_amdgcn_sched_barrier(0);
     }
   __syncthreads();
-  const int orow0 = row0 + 128 * wr, ocol0 = col0 + 128 * wc;
+  const int orow0 = row0 + 64 * wr, ocol0 = col0 + 128 * wc;
   uint16_t *hih = hi + (size_t)bh * T * F;
 #pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
+  for (int it = 0; it < 16; ++it) {
     const int piece = it * 64 + lane;  // 16 pieces of 8 columns per row
     const int rr = piece >> 4, c8 = (piece & 15) * 8;
     const int row = orow0 + rr, col = ocol0 + c8;
@@ -384,7 +383,7 @@ void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStr
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   const int RT = (p.T + MG_BM - 1) / MG_BM, CT = (p.F + MG_BN - 1) / MG_BN;
-  dim3 grid(p.BH * CT * RT), block(256);
+  dim3 grid(p.BH * CT * RT), block(512);
   if (p.d == 128)
     hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
   else
