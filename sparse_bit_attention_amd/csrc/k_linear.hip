@@ -36,21 +36,30 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t base = ((size_t)bh * N + (size_t)j * BLK) * D;
 
-  // stage V and K rows (zeros past the valid rows)
-  for (int x = tid; x < 64 * (D / 4); x += 256) {
+  // stage V and K rows (zeros past the valid rows); all loads are issued
+  // before any is used
+  constexpr int NX = 64 * (D / 4) / 256;  // 8-byte pieces per thread
+  uint2 vv[NX], kk[NX];
+#pragma unroll
+  for (int e = 0; e < NX; ++e) {
+    const int x = tid + 256 * e;
     const int r = x / (D / 4), c = (x - r * (D / 4)) * 4;
-    uint2 v = make_uint2(0u, 0u), k = make_uint2(0u, 0u);
-    if (r < n) {
-      v = *(const uint2 *)(V + base + (size_t)r * D + c);
-      if (LIN) k = *(const uint2 *)(K + base + (size_t)r * D + c);
-    }
+    const int rc = r < n ? r : n - 1;  // a valid row; zeroed below
+    vv[e] = *(const uint2 *)(V + base + (size_t)rc * D + c);
+    if (LIN) kk[e] = *(const uint2 *)(K + base + (size_t)rc * D + c);
+  }
+#pragma unroll
+  for (int e = 0; e < NX; ++e) {
+    const int x = tid + 256 * e;
+    const int r = x / (D / 4), c = (x - r * (D / 4)) * 4;
+    const bool ok = r < n;
     uint32_t *dv = (uint32_t *)(sv + r * P + c);  // 4-byte aligned: P even, c even
-    dv[0] = v.x;
-    dv[1] = v.y;
+    dv[0] = ok ? vv[e].x : 0u;
+    dv[1] = ok ? vv[e].y : 0u;
     if (LIN) {
       uint32_t *dk = (uint32_t *)(sk + r * P + c);
-      dk[0] = k.x;
-      dk[1] = k.y;
+      dk[0] = ok ? kk[e].x : 0u;
+      dk[1] = ok ? kk[e].y : 0u;
     }
   }
   __syncthreads();

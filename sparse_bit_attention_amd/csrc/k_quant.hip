@@ -42,18 +42,31 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
 
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, amax = 0.f;
   uint2 vals[BLK];
+  auto accum = [&](uint2 v) {
+    const float a = bf2f(v.x & 0xFFFF), b = bf2f(v.x >> 16), c = bf2f(v.y & 0xFFFF), d = bf2f(v.y >> 16);
+    s0 = s0 + a;
+    s1 = s1 + b;
+    s2 = s2 + c;
+    s3 = s3 + d;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
+  };
+  if (n == BLK) {
+    // full block (all but a head's last): every load is unconditional, so
+    // they are all in flight at once; lanes without channels read channels
+    // 0..3 of the same row (values already present: the block max is
+    // unchanged, and their sums are not stored)
+    const size_t base_c = base - 4 * cl + 4 * (cl < LPT ? cl : 0);
 #pragma unroll
-  for (int r = 0; r < BLK; ++r) {
-    uint2 v = make_uint2(0u, 0u);
-    if (act && r < n) v = *(const uint2 *)(X + base + (size_t)r * D);
-    vals[r] = v;
-    if (act && r < n) {
-      float a = bf2f(v.x & 0xFFFF), b = bf2f(v.x >> 16), c = bf2f(v.y & 0xFFFF), d = bf2f(v.y >> 16);
-      s0 = s0 + a;
-      s1 = s1 + b;
-      s2 = s2 + c;
-      s3 = s3 + d;
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
+    for (int r = 0; r < BLK; ++r) vals[r] = *(const uint2 *)(X + base_c + (size_t)r * D);
+#pragma unroll
+    for (int r = 0; r < BLK; ++r) accum(vals[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < BLK; ++r) {
+      uint2 v = make_uint2(0u, 0u);
+      if (act && r < n) v = *(const uint2 *)(X + base + (size_t)r * D);
+      vals[r] = v;
+      if (act && r < n) accum(v);
     }
   }
   if (act) {
@@ -143,12 +156,24 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
 
   float xs[STEPS][4];
   float amax = 0.f;
+  uint2 raw[STEPS];
+  if (n == BLK) {
+    // full block: unconditional loads, all in flight at once
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) raw[s] = *(const uint2 *)(K + base + (size_t)(s * RPI + r0) * D);
+  } else {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int r = s * RPI + r0;
+      raw[s] = make_uint2(0u, 0u);
+      if (live && r < n) raw[s] = *(const uint2 *)(K + base + (size_t)r * D);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int r = s * RPI + r0;
-    uint2 v = make_uint2(0u, 0u);
+    const uint2 v = raw[s];
     const bool ok = live && r < n;
-    if (ok) v = *(const uint2 *)(K + base + (size_t)r * D);
     xs[s][0] = bf2f(v.x & 0xFFFF) - m4.x;
     xs[s][1] = bf2f(v.x >> 16) - m4.y;
     xs[s][2] = bf2f(v.y & 0xFFFF) - m4.z;
