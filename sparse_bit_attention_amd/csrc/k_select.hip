@@ -29,6 +29,7 @@ __device__ __forceinline__ uint32_t score_key(float v) {
 // the keys are in registers (E <= SEL_MAXE); otherwise every pass re-reads them
 // from LDS.
 constexpr int SEL_MAXE = 32;
+constexpr int SEL_HI = 12;  // key bits decided over all keys before the candidates are packed
 
 template <bool CACHED>
 struct RowKeys {
@@ -47,7 +48,7 @@ struct RowKeys {
 
 template <bool CACHED>
 __device__ void select_row_t(const float *srow, int T, int kb, uint64_t *mrow, uint64_t *mcol,
-                             int32_t *krow, int lane) {
+                             int32_t *krow, uint32_t *scratch, int lane) {
   constexpr int EMAX = CACHED ? SEL_MAXE : (1 << 30);
   const int E = (T + 63) >> 6;
   RowKeys<CACHED> rk;
@@ -60,9 +61,7 @@ __device__ void select_row_t(const float *srow, int T, int kb, uint64_t *mrow, u
   }
   // th = the kb-th largest key: the largest th with #{key >= th} >= kb,
   // built one bit at a time from the top.
-  uint32_t th = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
+  auto count_ge = [&](uint32_t cand) {
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < (CACHED ? SEL_MAXE : 1); ++e) {
@@ -72,7 +71,48 @@ __device__ void select_row_t(const float *srow, int T, int kb, uint64_t *mrow, u
         for (int x = 0; x < E; ++x) cnt += __popcll(__ballot(rk.get(x) >= cand));
       }
     }
-    if (cnt >= kb) th = cand;
+    return cnt;
+  };
+  uint32_t th = 0u;
+  int bit = 31;
+  if constexpr (CACHED) {
+    // The top SEL_HI bits over all keys; then usually few keys share that
+    // prefix P: count(key >= cand) = #(prefix > P) + #(prefix == P, key >=
+    // cand), and the candidates fit one register per lane (packed through
+    // the wave's LDS scratch), so the low bits cost one ballot per step.
+    for (; bit >= 32 - SEL_HI; --bit) {
+      const uint32_t cand = th | (1u << bit);
+      if (count_ge(cand) >= kb) th = cand;
+    }
+    const uint32_t P = th >> (32 - SEL_HI);
+    const int above = (P == (1u << SEL_HI) - 1u) ? 0 : count_ge((P + 1u) << (32 - SEL_HI));
+    int ncand = 0;
+#pragma unroll
+    for (int e = 0; e < SEL_MAXE; ++e)
+      if (e < E) ncand += __popcll(__ballot((rk.get(e) >> (32 - SEL_HI)) == P));
+    if (ncand <= 64) {
+      int pos = 0;
+#pragma unroll
+      for (int e = 0; e < SEL_MAXE; ++e) {
+        if (e < E) {
+          const bool c = (rk.get(e) >> (32 - SEL_HI)) == P;
+          const uint64_t m = __ballot(c);
+          if (c) scratch[pos + __popcll(m & ((1ull << lane) - 1ull))] = rk.get(e);
+          pos += __popcll(m);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t cv = lane < ncand ? scratch[lane] : 0u;  // 0 never reaches a candidate
+      __builtin_amdgcn_wave_barrier();
+      for (; bit >= 0; --bit) {
+        const uint32_t cand = th | (1u << bit);
+        if (above + __popcll(__ballot(cv >= cand)) >= kb) th = cand;
+      }
+    }
+  }
+  for (; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    if (count_ge(cand) >= kb) th = cand;
   }
   int need = kb;  // ties at th still to take, lowest index first
   int pos = 0;
@@ -114,9 +154,10 @@ __device__ void select_row_t(const float *srow, int T, int kb, uint64_t *mrow, u
   (void)EMAX;
 }
 
-// mrow: the row's W64 words; mcol (may be null): word e goes to mcol[e * T]
+// mrow: the row's W64 words; mcol (may be null): word e goes to mcol[e * T];
+// scratch: 64 words of LDS owned by the wave
 __device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, uint64_t *mcol,
-                           int32_t *krow, int lane) {
+                           int32_t *krow, uint32_t *scratch, int lane) {
   const int E = (T + 63) >> 6;
   if (kb <= 0) {
     for (int e = lane; e < E; e += 64) {
@@ -126,9 +167,9 @@ __device__ void select_row(const float *srow, int T, int kb, uint64_t *mrow, uin
     return;
   }
   if (E <= SEL_MAXE)
-    select_row_t<true>(srow, T, kb, mrow, mcol, krow, lane);
+    select_row_t<true>(srow, T, kb, mrow, mcol, krow, scratch, lane);
   else
-    select_row_t<false>(srow, T, kb, mrow, mcol, krow, lane);
+    select_row_t<false>(srow, T, kb, mrow, mcol, krow, scratch, lane);
 }
 
 template <int D>
@@ -142,6 +183,7 @@ __global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ q
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float *sq = smem;          // [R][D]
   float *ss = smem + R * D;  // [R][T]
+  uint32_t *scr = (uint32_t *)(ss + R * T);  // [4 waves][64]
   const int groups = (T + R - 1) / R;
   const int bh = blockIdx.x / groups;
   const int i0 = (blockIdx.x - bh * groups) * R;
@@ -163,7 +205,25 @@ __global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ q
         kt[4 * c + 2] = a.z - m.z;
         kt[4 * c + 3] = a.w - m.w;
       }
-      for (int r = 0; r < nr; ++r) {
+      // four rows at a time: four independent FMA chains, each in channel order
+      int r = 0;
+      for (; r + 4 <= nr; r += 4) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float4 q = ((const float4 *)(sq + (r + u) * D))[c];
+            acc[u] = __builtin_fmaf(q.x, kt[4 * c + 0], acc[u]);
+            acc[u] = __builtin_fmaf(q.y, kt[4 * c + 1], acc[u]);
+            acc[u] = __builtin_fmaf(q.z, kt[4 * c + 2], acc[u]);
+            acc[u] = __builtin_fmaf(q.w, kt[4 * c + 3], acc[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ss[(r + u) * T + j] = acc[u];
+      }
+      for (; r < nr; ++r) {
         const float4 *qr = (const float4 *)(sq + r * D);
         float acc = 0.0f;
 #pragma unroll
@@ -184,14 +244,14 @@ __global__ __launch_bounds__(256) void k_scores_topk(const float *__restrict__ q
     const size_t row = (size_t)bh * T + i0 + r;
     uint64_t *mcol = maskt ? maskt + (size_t)bh * W64 * T + i0 + r : nullptr;
     select_row(ss + r * T, T, kb, mask + row * W64, mcol, kept + row * (size_t)(kb > 0 ? kb : 1),
-               lane);
+               scr + 64 * w, lane);
   }
 }
 
 void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   const int R = p.rows_sel;
   const int groups = (p.T + R - 1) / R;
-  const size_t lds = sizeof(float) * (size_t)R * (p.d + p.T);
+  const size_t lds = sizeof(float) * (size_t)R * (p.d + p.T) + 4 * 64 * sizeof(uint32_t);
   dim3 grid(p.BH * groups), block(256);
   if (p.d == 128)
     hipLaunchKernelGGL(k_scores_topk<128>, grid, block, lds, st, ws.qbar, ws.kbar, ws.mu, p.T, R,

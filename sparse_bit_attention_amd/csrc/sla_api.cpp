@@ -41,10 +41,11 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   return w;
 }
 
-// Rows of query blocks per selection workgroup: R*(d + T) floats must fit in
-// 64 KiB of LDS; a multiple of 4 (one row per wave) when possible.
+// Rows of query blocks per selection workgroup: R*(d + T) floats plus 1 KiB
+// of per-wave scratch must fit in 64 KiB of LDS; a multiple of 4 (one row per
+// wave) when possible.
 static int selection_rows(int d, int T) {
-  long r = (64L * 1024 / 4) / (long)(d + T);
+  long r = ((64L * 1024 - 1024) / 4) / (long)(d + T);
   if (r > 16) r = 16;
   if (r >= 4) r &= ~3L;
   return (int)r;

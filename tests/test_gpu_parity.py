@@ -115,8 +115,8 @@ def assert_close(got, ref, label):
         assert mx == 0.0
 
 
-def full_compare(wl, sm_scale=0.0):
-    m, o, dv, inputs = run(wl, sm_scale=sm_scale)
+def full_compare(wl, sm_scale=0.0, inputs=None):
+    m, o, dv, inputs = run(wl, inputs=inputs, sm_scale=sm_scale)
     q, k, v, w = inputs
     out = host_u16(o)
     scale = sm_scale if sm_scale > 0 else None
@@ -153,6 +153,27 @@ SMALL = [
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
 def test_small_full_parity(wl):
     full_compare(wl)
+
+
+def tied_inputs(wl, period):
+    """Synthetic inputs whose K block j repeats K block j % period: key blocks
+    with equal means give equal scores, so every row has ties at its
+    threshold (broken towards the lower block index)."""
+    q, k, v, w = synth.all_inputs(wl)
+    k = k.copy()
+    for j in range(period, wl.T):
+        n = min(64, wl.N - 64 * j)
+        s = j % period
+        k[:, :, 64 * j:64 * j + n] = k[:, :, 64 * s:64 * s + n]
+    return q, k, v, w
+
+
+@pytest.mark.parametrize("period", [3, 40])
+def test_tied_block_scores(period):
+    # period 3: a third of all scores share each value (many candidates at
+    # the threshold); period 40: pairs of equal scores near the threshold
+    wl = synth.Workload(f"ties-{period}", 1, 2, 64 * 64, 128, 0.3, seed=13)
+    full_compare(wl, inputs=tied_inputs(wl, period))
 
 
 def test_explicit_sm_scale():
