@@ -18,22 +18,53 @@
 
 namespace sla {
 
-// One workgroup (4 waves) per key block.  LDS: V and phi(K) as bf16 rows with
-// an odd dword pitch (bank-conflict free column reads).
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+
+// Four consecutive rows k0 .. k0+3 of column n0 + l%16 of a row-major bf16
+// LDS tile (pitch in elements), by the transposing LDS read: lane j of each
+// 16-lane group supplies row k0 + j/4, columns n0 + 4(j%4) .. +3.
+__device__ __forceinline__ uint2 lds_col4(const uint16_t *tile, int pitch, int k0, int n0,
+                                          int lane) {
+  const int j = lane & 15;
+  const uint16_t *a = tile + (k0 + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16 *)a);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// MFMA operand (16x16x32 bf16, k order of kmaj_off) of the 16 columns n0 ..
+// n0+15 and the 32 keys 32 kc2 .. of a row-major [key][column] LDS tile: lane
+// (column n0 + l%16, group g = l/16) holds keys 32 kc2 + 4g + 0..3 and
+// 32 kc2 + 16 + 4g + 0..3.
+__device__ __forceinline__ v4u lds_frag(const uint16_t *tile, int pitch, int kc2, int n0, int lane) {
+  const int g = lane >> 4;
+  const uint2 lo = lds_col4(tile, pitch, 32 * kc2 + 4 * g, n0, lane);
+  const uint2 hi = lds_col4(tile, pitch, 32 * kc2 + 16 + 4 * g, n0, lane);
+  return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
+// One workgroup (4 waves) per key block.  LDS: V and phi(K) as row-major bf16
+// [key][channel] tiles; the pitch (D + 16 elements) keeps the rows 8-byte
+// aligned and puts four consecutive rows on distinct banks, so operand
+// fragments come straight from the transposing read.  The state is computed
+// as H = phi(K)^T V (rows: phi channel c, columns: value channel c2), whose
+// accumulators hold four consecutive c per lane: one 8-byte store each into
+// the hstate_off order.
 template <int D, bool LIN>
 __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
                                                  const uint16_t *__restrict__ V, int N, int T,
                                                  int F, uint16_t *__restrict__ vt,
                                                  uint16_t *__restrict__ hb) {
-  constexpr int P = D + 2;  // row pitch in bf16 (odd number of dwords)
+  constexpr int P = D + 16;  // row pitch in bf16
   constexpr int CG = D / 16;
   constexpr int KC32 = D / 32;
+  constexpr int MT = CG / 4;  // row tiles (16 phi channels) per wave
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 64 * P];
   uint16_t *sv = smem, *sk = smem + 64 * P;
   const int blk = blockIdx.x;
   const int bh = blk / T, j = blk - bh * T;
   const int n = min(BLK, N - j * BLK);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
   const size_t base = ((size_t)bh * N + (size_t)j * BLK) * D;
 
   // stage V and K rows (zeros past the valid rows); all loads are issued
@@ -53,119 +84,99 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
     const int x = tid + 256 * e;
     const int r = x / (D / 4), c = (x - r * (D / 4)) * 4;
     const bool ok = r < n;
-    uint32_t *dv = (uint32_t *)(sv + r * P + c);  // 4-byte aligned: P even, c even
-    dv[0] = ok ? vv[e].x : 0u;
-    dv[1] = ok ? vv[e].y : 0u;
-    if (LIN) {
-      uint32_t *dk = (uint32_t *)(sk + r * P + c);
-      dk[0] = ok ? kk[e].x : 0u;
-      dk[1] = ok ? kk[e].y : 0u;
-    }
+    *(uint2 *)(sv + r * P + c) = ok ? vv[e] : make_uint2(0u, 0u);
+    if (LIN) *(uint2 *)(sk + r * P + c) = ok ? kk[e] : make_uint2(0u, 0u);
   }
   __syncthreads();
 
-  // phi(K) rows in float32, one lane per row, rounded to bf16 in place;
-  // padding rows become 0.
-  if (LIN && w == 0) {
-    const int r = lane;
-    uint16_t *row = sk + r * P;
-    if (r < n) {
-      float mx = -INFINITY;
-      for (int c = 0; c < D; ++c) mx = fmaxf(mx, bf2f(row[c]));
-      float s = 0.f;
-      for (int c = 0; c < D; ++c) s += __expf(bf2f(row[c]) - mx);
-      const float inv = 1.0f / s;
-      for (int c = 0; c < D; ++c) row[c] = f2bf(__expf(bf2f(row[c]) - mx) * inv);
-    } else {
-      for (int c = 0; c < D; ++c) row[c] = 0;
-    }
-  }
-  __syncthreads();
-
-  // V in kmaj order: fragment (kc2, cg), lane holds channel 16cg + lane%16 and
-  // the 8 keys 32kc2 + 16(e/4) + 4(lane/16) + e%4.
-  const int g = lane >> 4, l16 = lane & 15;
-  uint16_t *vdst = vt + (size_t)blk * BLK * D;
-  for (int f = w; f < 2 * CG; f += 4) {
-    const int kc2 = f / CG, cg = f - kc2 * CG;
-    const int c = 16 * cg + l16;
-    uint32_t pk[4];
+  // phi(K) rows in float32, rounded to bf16 in place; four threads per row
+  // (D/4 channels each, max and sum combined by shuffles); padding rows
+  // become 0.
+  if (LIN) {
+    constexpr int CPT = D / 4;
+    const int r = tid >> 2, part = tid & 3;
+    uint16_t *row = sk + r * P + part * CPT;
+    float x[CPT];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int e0 = 2 * h, e1 = 2 * h + 1;
-      const int s0 = 32 * kc2 + 16 * (e0 >> 2) + 4 * g + (e0 & 3);
-      const int s1 = 32 * kc2 + 16 * (e1 >> 2) + 4 * g + (e1 & 3);
-      pk[h] = (uint32_t)sv[s0 * P + c] | ((uint32_t)sv[s1 * P + c] << 16);
+    for (int c = 0; c < CPT; c += 2) {
+      const uint32_t two = *(const uint32_t *)(row + c);
+      x[c] = bf2f((uint16_t)(two & 0xFFFF));
+      x[c + 1] = bf2f((uint16_t)(two >> 16));
     }
-    *(uint4 *)(vdst + ((size_t)f * 64 + lane) * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) mx = fmaxf(mx, x[c]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    float sm = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      x[c] = __expf(x[c] - mx);
+      sm += x[c];
+    }
+    sm += __shfl_xor(sm, 1, 64);
+    sm += __shfl_xor(sm, 2, 64);
+    const float inv = r < n ? 1.0f / sm : 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 2)
+      *(uint32_t *)(row + c) = pack2bf(x[c] * inv, x[c + 1] * inv);
   }
+  __syncthreads();
+
+  // V fragments (value channels 16 bt .., keys 32 kc2 ..) in the kmaj order
+  // the attention kernel reads: B operands here, written out as they are;
+  // wave w writes fragments f = kc2 * CG + bt with f % 4 == w
+  v4u vf[2][CG];
+#pragma unroll
+  for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+    for (int bt = 0; bt < CG; ++bt) vf[kc2][bt] = lds_frag(sv, P, kc2, 16 * bt, lane);
+  uint16_t *vdst = vt + (size_t)blk * BLK * D;
+#pragma unroll
+  for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+    for (int bt = 0; bt < CG; ++bt)
+      if (((kc2 * CG + bt) & 3) == w)
+        *(v4u *)(vdst + ((size_t)(kc2 * CG + bt) * 64 + lane) * 8) = vf[kc2][bt];
   if (!LIN) return;
 
-  // Hb^T[c2][c] = sum_s V[s][c2] phi(K)[s][c]: A = V^T fragments (as above),
-  // B = phi(K) fragments with the same key order.  Wave w owns rows
-  // c2 in [D/4 * w, D/4 * (w+1)).
-  constexpr int MT = CG / 4;  // row tiles per wave
-  v4f acc[MT][CG];
+  // H[c][c2] = sum_s phi(K)[s][c] V[s][c2], z[c] = sum_s phi(K)[s][c]: wave w
+  // owns the phi rows 16 (MT w + a) .. +15, all value columns and a ones column
+  v4f acc[MT][CG], accz[MT];
 #pragma unroll
-  for (int a = 0; a < MT; ++a)
+  for (int a = 0; a < MT; ++a) {
+    accz[a] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < CG; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int bt = 0; bt < CG; ++bt) acc[a][bt] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const v4u ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-  for (int kc2 = 0; kc2 < 2; ++kc2) {
-    v4u af[MT], bf[CG];
+  for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
-      const int c = 16 * (w * MT + a) + l16;
-      uint32_t pk[4];
+      const v4u af = lds_frag(sk, P, kc2, 16 * (MT * w + a), lane);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int e0 = 2 * h, e1 = 2 * h + 1;
-        const int s0 = 32 * kc2 + 16 * (e0 >> 2) + 4 * g + (e0 & 3);
-        const int s1 = 32 * kc2 + 16 * (e1 >> 2) + 4 * g + (e1 & 3);
-        pk[h] = (uint32_t)sv[s0 * P + c] | ((uint32_t)sv[s1 * P + c] << 16);
-      }
-      af[a] = v4u{pk[0], pk[1], pk[2], pk[3]};
+      for (int bt = 0; bt < CG; ++bt) acc[a][bt] = mfma_bf16(af, vf[kc2][bt], acc[a][bt]);
+      accz[a] = mfma_bf16(af, ones, accz[a]);
     }
+  // accumulator (a, bt) register r: c = 16 (MT w + a) + 4g + r, c2 = 16 bt + l16;
+  // the four c of a lane are consecutive elements of hstate_off, and a wave's
+  // stores of one tile fill 512 contiguous bytes
+  uint16_t *ho = hb + (size_t)blk * F;
 #pragma unroll
-    for (int b = 0; b < CG; ++b) {
-      const int c = 16 * b + l16;
-      uint32_t pk[4];
+  for (int a = 0; a < MT; ++a) {
+    const int c0 = 16 * (MT * w + a) + 4 * g;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int e0 = 2 * h, e1 = 2 * h + 1;
-        const int s0 = 32 * kc2 + 16 * (e0 >> 2) + 4 * g + (e0 & 3);
-        const int s1 = 32 * kc2 + 16 * (e1 >> 2) + 4 * g + (e1 & 3);
-        pk[h] = (uint32_t)sk[s0 * P + c] | ((uint32_t)sk[s1 * P + c] << 16);
-      }
-      bf[b] = v4u{pk[0], pk[1], pk[2], pk[3]};
+    for (int bt = 0; bt < CG; ++bt) {
+      const int c2 = 16 * bt + l16;
+      *(uint2 *)(ho + hstate_off(c0, c2, KC32)) =
+          make_uint2(pack2bf(acc[a][bt][0], acc[a][bt][1]), pack2bf(acc[a][bt][2], acc[a][bt][3]));
     }
-#pragma unroll
-    for (int a = 0; a < MT; ++a)
-#pragma unroll
-      for (int b = 0; b < CG; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
+    if (l16 == 0)
+      *(uint2 *)(ho + D * D + c0) =
+          make_uint2(pack2bf(accz[a][0], accz[a][1]), pack2bf(accz[a][2], accz[a][3]));
   }
-  // z[c] = sum over rows of the bf16 phi values (same values the product used)
-  float zc = 0.f;
-  if (tid < D)
-    for (int r = 0; r < BLK; ++r) zc += bf2f(sk[r * P + tid]);
-  __syncthreads();  // done reading sv/sk: reuse as the output stage
-  uint16_t *so = smem;  // F bf16 values (F <= 2*64*P)
-#pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int b = 0; b < CG; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c2 = 16 * (w * MT + a) + 4 * g + r;  // accumulator row
-        const int c = 16 * b + l16;                    // accumulator column
-        so[hstate_off(c, c2, KC32)] = f2bf(acc[a][b][r]);
-      }
-  if (tid < D) so[D * D + tid] = f2bf(zc);
-  for (int x = D * D + D + tid; x < F; x += 256) so[x] = 0;
-  __syncthreads();
-  uint4 *dst = (uint4 *)(hb + (size_t)blk * F);
-  const uint4 *src = (const uint4 *)so;
-  for (int x = tid; x < F / 8; x += 256) dst[x] = src[x];
+  for (int x = D * D + D + tid; x < F; x += 256) ho[x] = 0;
 }
 
 // Projection W [d_out][d_in] into wfrag_off order (A operand, k = d_in).
