@@ -194,67 +194,78 @@ __global__ void k_w_swizzle(const uint16_t *__restrict__ W, int D, uint16_t *__r
 // other's waits) owns a 256 x 256 output tile; wave w owns rows 64 (w/2) ..
 // +63 and columns 128 (w%2) .. +127 in 8 accumulator tiles.  Per step of 32
 // key blocks:
-//  * A (the complement mask as bf16 ones and zeros) is built by each wave in
-//    registers, straight from its rows' mask words;
+//  * A (the complement mask as bf16 ones and zeros) is built by each wave
+//    from its rows' mask words, four keys at a time through a 16-entry table
+//    of bf16 patterns in LDS;
 //  * B (32 Hb rows x 256 columns) is staged in LDS in MFMA fragment order:
 //    thread (w, l) loads keys 4w .. 4w+3 of columns 4l .. 4l+3 and writes
 //    half of each of those columns' 16-byte fragment slots.  Slots are
 //    XOR-swizzled by their 8-slot group, so both the writes and the fragment
 //    reads spread over all banks.
-// Global loads run two steps ahead; B is double-buffered in LDS.  The row
-// tiles of one column tile run one after another on one XCD, so each Hb
-// column slice comes from HBM once.
+// Pipeline (step s): issue the global loads of step s+3, read step s+1's B
+// fragments into registers, run step s's products from registers, then
+// store step s+2's B (loaded one step earlier) into LDS.  B is triple-buffered
+// in LDS, so one barrier per step suffices, and the products never wait for
+// LDS.  The row tiles of one column tile run one after another on one XCD,
+// so each Hb column slice comes from HBM once.
 constexpr int MG_BM = 256;  // rows per workgroup
 constexpr int MG_BN = 256;  // columns per workgroup
 constexpr int MG_BK = 32;   // key blocks per step
 
-// 8 mask bits (keys k .. k+7, bit i = key k+i, 1 = use the block) as the four
-// dwords of an MFMA operand: dword h holds key 2h (low half) and 2h+1 (high
-// half) as bf16 1.0 or 0.  Even keys go to bits 0,2,4,6, odd keys to bits
-// 16,18,20,22; bit pair h times (0x3F80 >> 2h) is then dword h.
-__device__ __forceinline__ v4u bits_to_bf16x8(uint32_t by) {
-  const uint32_t y = (by & 0x55u) | (((by >> 1) & 0x55u) << 16);
-  return v4u{(uint32_t)__umul24(y & 0x00010001u, 0x3F80u), (uint32_t)__umul24(y & 0x00040004u, 0x3F80u >> 2),
-             (uint32_t)__umul24(y & 0x00100010u, 0x3F80u >> 4), (uint32_t)__umul24(y & 0x00400040u, 0x3F80u >> 6)};
-}
-
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict__ maskt,
                                                      const uint16_t *__restrict__ hb, int T,
-                                                     int W64, int F, uint16_t *__restrict__ hi) {
-  // two B buffers of 16 KiB; the epilogue reuses all 128 KiB to stage each
+                                                     int W64, int F, int ntiles,
+                                                     uint16_t *__restrict__ hi) {
+  // three B buffers of 16 KiB; the epilogue reuses all 128 KiB to stage each
   // wave's bf16 tile
-  __shared__ __attribute__((aligned(16))) uint4 smem[8192];
+  // lds[0..8): the table, nibble n (keys k .. k+3, bit i = key k+i) as four
+  // bf16 ones and zeros (at LDS address 0, so a table offset is an address)
+  __shared__ __attribute__((aligned(16))) uint4 lds[8 + 8192];
+  uint2 *lut = (uint2 *)lds;
+  uint4 *smem = lds + 8;
   const int RT = (T + MG_BM - 1) / MG_BM, CT = (F + MG_BN - 1) / MG_BN;
-  int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int rt = b % RT;
-  b /= RT;
-  const int ct = b % CT;
-  const int bh = b / CT;
-  const int row0 = rt * MG_BM, col0 = ct * MG_BN;
+  // Tiles in the order (head, column tile, row tile), row tile fastest; XCD x
+  // (= blockIdx.x % 8) owns one contiguous eighth of that order and its
+  // workgroups take every L-th tile of it, so the row tiles of a column tile
+  // run close together in time on one XCD and share its L2.
+  const int xcd = blockIdx.x & 7, L = gridDim.x >> 3;
+  const int tq = ntiles >> 3, tr = ntiles & 7;
+  const int tbeg = xcd * tq + min(xcd, tr), tcnt = tq + (xcd < tr ? 1 : 0);
+  int li = blockIdx.x >> 3;
+  if (li >= tcnt) return;  // no barriers before this point
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = w >> 1, wc = w & 1;
-  const uint16_t *hbh = hb + (size_t)bh * T * F;
-  const uint64_t *mh = maskt + (size_t)bh * W64 * T;  // word-major: [W64][T]
+  const int kshift = 8 * (lane >> 5);
+  if (tid < 16)  // visible after the first tile's first barrier
+    lut[tid] = make_uint2(((tid & 1) ? 0x3F80u : 0u) | ((tid & 2) ? 0x3F800000u : 0u),
+                          ((tid & 4) ? 0x3F80u : 0u) | ((tid & 8) ? 0x3F800000u : 0u));
 
-  // ---- A: lane l owns rows 64 wr + 32 x + l%32 (x < 2) and keys 8 (l/32) ..
-  // +7 of each 16-key half-step.  Rows past T read row T-1 (their outputs are
-  // never stored).
-  int arow[2];
+  // ---- the current tile: A lane l owns rows 64 wr + 32 x + l%32 (x < 2) and
+  // keys 8 (l/32) .. +7 of each 16-key half-step; rows past T read row T-1
+  // (their outputs are never stored).  B: thread (w, l) holds keys 4w .. 4w+3
+  // of columns 4l .. 4l+3; keys past T read row T-1 (their A entries are 0),
+  // columns past F read the last four columns (never stored).
+  int bh = 0, row0 = 0, col0 = 0, arow[2], bcol = 0;
+  const uint16_t *hbh = hb;
+  const uint64_t *mh = maskt;  // word-major: [W64][T]
+  auto set_tile = [&](int t) {
+    const int rt = t % RT, r2 = t / RT;
+    col0 = (r2 % CT) * MG_BN;
+    bh = r2 / CT;
+    row0 = rt * MG_BM;
+    hbh = hb + (size_t)bh * T * F;
+    mh = maskt + (size_t)bh * W64 * T;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) arow[x] = min(row0 + 64 * wr + 32 * x + (lane & 31), T - 1);
+    for (int x = 0; x < 2; ++x) arow[x] = min(row0 + 64 * wr + 32 * x + (lane & 31), T - 1);
+    bcol = min(col0 + 4 * lane, F - 4);
+  };
   auto load_words = [&](int word, uint64_t (&wd)[2]) {
     word = min(word, W64 - 1);
 #pragma unroll
     for (int x = 0; x < 2; ++x) wd[x] = mh[(size_t)word * T + arow[x]];
   };
-  const int kshift = 8 * (lane >> 5);
-
-  // ---- B: thread (w, l) holds keys 4w .. 4w+3 of columns 4l .. 4l+3.  Keys
-  // past T read row T-1 (their A entries are 0); columns past F read the last
-  // four columns (never stored).
-  const int bcol = min(col0 + 4 * lane, F - 4);
   auto load_b = [&](int s, uint2 (&v)[4]) {
     const int j0 = s * MG_BK + 4 * w;
 #pragma unroll
@@ -287,97 +298,136 @@ __global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict_
   const int rslot = lane ^ ((lane >> 3) & 7);
 
   v16f acc[2][4];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  // one step: A from the mask words, B from LDS buffer cur
-  auto mma_step = [&](int s, const uint64_t (&wd)[2], const uint4 *cur) {
+  // B fragments of one step: [ks][y], column tile 4 wc + y
+  auto read_b = [&](const uint4 *buf, v4u (&bf)[2][4]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) bf[ks][y] = __builtin_bit_cast(v4u, buf[((4 * wc + y) * 2 + ks) * 64 + rslot]);
+  };
+  // one step: A from the mask words, B from registers
+  auto mma_step = [&](int s, const uint64_t (&wd)[2], const v4u (&bf)[2][4]) {
     const int j0 = s * MG_BK;
     const int nvalid = T - j0;  // key blocks past T contribute nothing
     const uint32_t valid = nvalid >= 32 ? ~0u : (nvalid > 0 ? (1u << nvalid) - 1u : 0u);
-    uint32_t t[2];
+    // the four nibbles of a lane's keys (half-step ks, keys 8 (l/32) .. +7)
+    // as byte offsets into the table: byte 2 ks + h = nibble h of byte ks, x 8
+    uint32_t u[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) t[x] = ((~(uint32_t)(wd[x] >> (j0 & 32))) & valid) >> kshift;
+    for (int x = 0; x < 2; ++x) {
+      const uint32_t t = ((~(uint32_t)(wd[x] >> (j0 & 32))) & valid) >> kshift;
+      u[x] = ((t & 0x000F000Fu) << 3) | ((t & 0x00F000F0u) << 7);
+    }
+    const char *lb = (const char *)lut;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v4u af[2], bf[4];
+      v4u af[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) af[x] = bits_to_bf16x8((t[x] >> (16 * ks)) & 0xFFu);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) bf[y] = __builtin_bit_cast(v4u, cur[((4 * wc + y) * 2 + ks) * 64 + rslot]);
+      for (int x = 0; x < 2; ++x) {
+        const uint2 lo = *(const uint2 *)(lb + __builtin_amdgcn_ubfe(u[x], 16 * ks, 8));
+        const uint2 hi2 = *(const uint2 *)(lb + __builtin_amdgcn_ubfe(u[x], 16 * ks + 8, 8));
+        af[x] = v4u{lo.x, lo.y, hi2.x, hi2.y};
+      }
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = mfma32_bf16(af[x], bf[y], acc[x][y]);
+        for (int y = 0; y < 4; ++y) acc[x][y] = mfma32_bf16(af[x], bf[ks][y], acc[x][y]);
     }
   };
+  auto nxt = [](int i) { return i == 2 ? 0 : i + 1; };
 
-  // Steps in pairs (an even count; a step past T has an all-zero A): the two
-  // B register sets and the mask words keep fixed names, loaded two steps
-  // (the words: one pair) ahead.
+  // Steps in pairs (an even count; a step past T has an all-zero A, and
+  // loads past the last step read clamped rows): the staging registers, the
+  // B fragment sets and the mask words keep fixed names.
   const int steps = (((T + MG_BK - 1) / MG_BK) + 1) & ~1;
-  uint2 bvA[4], bvB[4];
+  uint2 gA[4], gB[4];        // global staging: steps of even / odd index
+  v4u bf0[2][4], bf1[2][4];  // B fragments: steps of even / odd index
   uint64_t wdc[2], wdn[2];
-  uint4 *buf0 = smem, *buf1 = smem + 1024;
-  {
-    uint2 b0[4];
-    load_b(0, b0);
-    load_b(1, bvA);
-    load_words(0, wdc);
-    store_b(b0, buf0);
-  }
-  __syncthreads();
-  for (int s = 0; s < steps; s += 2) {
-    // even step s: B buffer 0, words wdc (steps s, s+1).  The fences keep the
-    // transposing stores (which wait for their loads) after the products.
-    load_b(s + 2, bvB);
-    load_words((s + 2) >> 1, wdn);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step(s, wdc, buf0);
-    __builtin_amdgcn_sched_barrier(0);
-    store_b(bvA, buf1);
+  // the first tile's first loads; a later tile's are issued before the
+  // previous tile's output stores, so those stores drain behind the next
+  // tile's products
+  set_tile(tbeg + li);
+  load_b(0, gA);
+  load_b(1, gB);
+  load_words(0, wdc);
+  for (; li < tcnt; li += L) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+    store_b(gA, smem);
+    store_b(gB, smem + 1024);
+    load_b(2, gA);
     __syncthreads();
-    // odd step s+1: B buffer 1
-    load_b(s + 3, bvA);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step(s + 1, wdc, buf1);
-    __builtin_amdgcn_sched_barrier(0);
-    store_b(bvB, buf0);
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 2; ++x) wdc[x] = wdn[x];
-  }
-
-  // epilogue: each wave stages its 64 x 128 tile as bf16 rows (256 B pitch),
-  // then writes 16-byte pieces of rows < T, columns < F
-  uint16_t *st = (uint16_t *)(smem + w * 1024);
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 32 * x + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int cc = 32 * y + (lane & 31);
-        st[rr * 128 + cc] = f2bf(acc[x][y][r]);
-      }
-      // one accumulator tile at a time (keeps the register demand small)
+    read_b(smem, bf0);
+    int bi = 0;  // LDS buffer of step s
+    for (int s = 0; s < steps; s += 2) {
+      int b1 = nxt(bi), b2 = nxt(b1);
+      // even step s
+      load_b(s + 3, gB);
+      load_words((s + 2) >> 1, wdn);
+      read_b(smem + 1024 * b1, bf1);
       __builtin_amdgcn_sched_barrier(0);
+      mma_step(s, wdc, bf0);
+      __builtin_amdgcn_sched_barrier(0);
+      store_b(gA, smem + 1024 * b2);
+      __syncthreads();
+      bi = b1;
+      b1 = b2;
+      b2 = nxt(b2);
+      // odd step s+1
+      load_b(s + 4, gA);
+      read_b(smem + 1024 * b1, bf0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(s + 1, wdc, bf1);
+      __builtin_amdgcn_sched_barrier(0);
+      store_b(gB, smem + 1024 * b2);
+      __syncthreads();
+      bi = b1;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) wdc[x] = wdn[x];
     }
-  __syncthreads();
-  const int orow0 = row0 + 64 * wr, ocol0 = col0 + 128 * wc;
-  uint16_t *hih = hi + (size_t)bh * T * F;
+
+    // epilogue: each wave stages its 64 x 128 tile as bf16 rows (256 B
+    // pitch), then writes 16-byte pieces of rows < T, columns < F
+    const int orow0 = row0 + 64 * wr, ocol0 = col0 + 128 * wc;
+    uint16_t *hih = hi + (size_t)bh * T * F;
+    if (li + L < tcnt) {
+      set_tile(tbeg + li + L);
+      load_b(0, gA);
+      load_b(1, gB);
+      load_words(0, wdc);
+    }
+    uint16_t *st = (uint16_t *)(smem + w * 1024);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          // registers r, r+1: rows rr, rr+1 of column cc
+          const int rr = 32 * x + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int cc = 32 * y + (lane & 31);
+          const uint32_t pr = pack2bf(acc[x][y][r], acc[x][y][r + 1]);
+          st[rr * 128 + cc] = (uint16_t)pr;
+          st[(rr + 1) * 128 + cc] = (uint16_t)(pr >> 16);
+        }
+        // one accumulator tile at a time (keeps the register demand small)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // the staging area is private to the wave: its own LDS ordering suffices
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int piece = it * 64 + lane;  // 16 pieces of 8 columns per row
-    const int rr = piece >> 4, c8 = (piece & 15) * 8;
-    const int row = orow0 + rr, col = ocol0 + c8;
-    if (row < T && col < F)
-      *(uint4 *)(hih + (size_t)row * F + col) = *(const uint4 *)(st + rr * 128 + c8);
+    for (int it = 0; it < 16; ++it) {
+      const int piece = it * 64 + lane;  // 16 pieces of 8 columns per row
+      const int rr = piece >> 4, c8 = (piece & 15) * 8;
+      const int row = orow0 + rr, col = ocol0 + c8;
+      if (row < T && col < F)
+        *(uint4 *)(hih + (size_t)row * F + col) = *(const uint4 *)(st + rr * 128 + c8);
+    }
+    __syncthreads();  // staging reads done before the next tile's B stores
   }
 }
 
@@ -403,11 +453,15 @@ void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStr
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   const int RT = (p.T + MG_BM - 1) / MG_BM, CT = (p.F + MG_BN - 1) / MG_BN;
-  dim3 grid(p.BH * CT * RT), block(512);
+  const int ntiles = p.BH * CT * RT;
+  // persistent: one workgroup per CU (256 CUs, 8 XCDs), fewer for small
+  // problems
+  const int nwg = std::min(256, 8 * ((ntiles + 7) / 8));
+  dim3 grid(nwg), block(512);
   if (p.d == 128)
-    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
+    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ntiles, ws.hi);
   else
-    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ws.hi);
+    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ntiles, ws.hi);
 }
 
 }  // namespace sla
