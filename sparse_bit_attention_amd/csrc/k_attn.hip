@@ -233,9 +233,8 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
 // ---------------------------------------------------------------------------
 // Software-pipelined loop of the bound path.  The kept blocks are walked as a
 // stream of 16-key tiles (sub-stage sigma = 4 n + t: block n, key tile t).
-// Sub-stage sigma issues three independent pieces of work, which the
-// scheduler interleaves so that vector ALU work runs while the matrix core is
-// busy:
+// Sub-stage sigma issues three independent pieces of work, interleaved in a
+// fixed order so that vector ALU work runs while the matrix core is busy:
 //   QK(sigma+1): S^T of tile sigma+1                         (int8 MFMA)
 //   SM(sigma):   probabilities of tile sigma, half a B fragment
 //   PV:          O^T += V^T P^T for the 32-key chunk finished two
@@ -257,20 +256,10 @@ struct Pipe {
   static constexpr int VLEAD = 4;        // V quarter sigma + VLEAD is loaded at sub-stage sigma
 };
 
-// Probabilities of one 16-key tile for one query tile: four scores in, two
-// bf16 pairs out (k order of kmaj_off), p = exp2(score * c + nm) cut to bf16
-// by keeping the upper half of each float32 (one byte permute per pair).  The
-// row sums are taken by the matrix core from the same bf16 values, so the
+// Probabilities: p = exp2(score * c + nm) cut to bf16 by keeping the upper
+// half of each float32, two per register in the k order of kmaj_off.  The row
+// sums are taken by the matrix core from the same bf16 values, so the
 // rounding of p enters numerator and denominator alike.
-__device__ __forceinline__ uint2 probs_tile(const v4i &s, float c, float nm) {
-  uint32_t x[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    x[r] = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[r]), c, nm)));
-  // bytes 2,3 of the first value, then bytes 2,3 of the second
-  return make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u));
-}
-
 // A fragment of 16 rows of bf16 ones: the rows of ones^T P^T are row sums of P.
 constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
 
@@ -308,53 +297,62 @@ __device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D
   for (int a = 0; a < VQ; ++a)
     st.vr[(R + P::VLEAD) % 8][a] = __builtin_bit_cast(v4u, vload_src[a * 64 + lane]);
   __builtin_amdgcn_sched_barrier(0);
-  // QK(sigma+1)
+  // The sub-stage's MFMAs in a fixed order: QK(sigma+1) (kc outer, so the
+  // two products into one score tile are four issues apart), the PV half,
+  // then the row sums on even R.  One score of SM(sigma) (fma + exp2) follows
+  // each of the first 16 MFMAs, and the byte permutes of a query tile follow
+  // its fourth score; a scheduling fence after each slot keeps this order, so
+  // the transcendental work is spread one per MFMA instead of clustered.
+  // SM(sigma): tile parity R & 1 fills half of chunk sigma/2's B fragment;
+  // PV: chunk sigma/2 - 1, channel tiles [VQ (R&1), VQ (R&1) + VQ), V quarter
+  // sigma-2.
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     st.s[(R + 1) & 1][u] = v4i{SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
+  constexpr int blk = R / 4;
+  constexpr int par = (R / 2) & 1;         // chunk being filled by SM
+  constexpr int par2 = ((R / 2) + 1) & 1;  // chunk consumed by PV
+  constexpr int vs = (R + 6) % 8;
+  constexpr int a0 = (R & 1) * VQ;
+  constexpr int NM = 4 * KC + 4 * VQ + ((R & 1) == 0 ? 4 : 0);
+  const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
+  const float c = pb.c[blk];
+  constexpr int NSLOT = NM > 16 ? NM : 16;  // d = 64 has fewer MFMAs than scores on odd R
+  uint32_t xs[4][4];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int i = 0; i < NSLOT; ++i) {
+    if (i >= NM) {
+      // no MFMA left in this slot
+    } else if (i < 4 * KC) {
+      const int kc = i / 4, u = i % 4;
       st.s[(R + 1) & 1][u] = mfma_i8(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
-  // SM(sigma): tile parity R & 1 fills half of chunk sigma/2's B fragment
-  {
-    constexpr int blk = R / 4;
-    constexpr int par = (R / 2) & 1;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint2 pp = probs_tile(st.s[R & 1][u], pb.c[blk], pb.nm[blk][u]);
-      if (R & 1) {
-        st.pf[par][u][2] = pp.x;
-        st.pf[par][u][3] = pp.y;
-      } else {
-        st.pf[par][u][0] = pp.x;
-        st.pf[par][u][1] = pp.y;
+    } else if (i < 4 * KC + 4 * VQ) {
+      const int j = i - 4 * KC, a = j / 4, u = j % 4;
+      st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par2][u], st.o[a0 + a][u]);
+    } else {
+      const int u = i - 4 * KC - 4 * VQ;
+      st.lacc[u] = mfma_bf16(ones, st.pf[par2][u], st.lacc[u]);
+    }
+    if (i < 16) {
+      // p = exp2(score * c + nm), cut to bf16 by keeping the upper half of
+      // the float32 (one byte permute per pair)
+      const int u = i / 4, r = i % 4;
+      xs[u][r] = __float_as_uint(
+          __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(st.s[R & 1][u][r]), c, pb.nm[blk][u])));
+      if (r == 3) {
+        // bytes 2,3 of the first value, then bytes 2,3 of the second
+        const uint32_t p0 = __builtin_amdgcn_perm(xs[u][1], xs[u][0], 0x07060302u);
+        const uint32_t p1 = __builtin_amdgcn_perm(xs[u][3], xs[u][2], 0x07060302u);
+        if (R & 1) {
+          st.pf[par][u][2] = p0;
+          st.pf[par][u][3] = p1;
+        } else {
+          st.pf[par][u][0] = p0;
+          st.pf[par][u][1] = p1;
+        }
       }
     }
-  }
-  // PV of chunk sigma/2 - 1, channel tiles [VQ (R&1), VQ (R&1) + VQ), V quarter sigma-2
-  {
-    constexpr int par = ((R / 2) + 1) & 1;
-    constexpr int vs = (R + 6) % 8;
-    constexpr int a0 = (R & 1) * VQ;
-#pragma unroll
-    for (int a = 0; a < VQ; ++a)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par][u], st.o[a0 + a][u]);
-    if ((R & 1) == 0) {
-      const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) st.lacc[u] = mfma_bf16(ones, st.pf[par][u], st.lacc[u]);
-    }
-  }
-  constexpr int NMFMA = 4 * KC + 4 * VQ + ((R & 1) == 0 ? 4 : 0);
-  constexpr int VALU_PER = (80 + NMFMA - 1) / NMFMA;
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
