@@ -382,15 +382,20 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     st.lacc[u] = v4f{0.f, 0.f, 0.f, 0.f};
     st.pf[1][u] = v4u{0u, 0u, 0u, 0u};  // chunk -1: zero probabilities
   }
-  // prologue: K tiles 0 .. KLEAD-1, V quarters 0 .. VLEAD-1
+  // prologue: K tiles 0 .. KLEAD-1, then V quarters 0 .. VLEAD-1, in this
+  // order (fenced): the loop's first sub-stages count on the K tiles being
+  // the oldest loads in flight, so their waits leave the later loads pending
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int x = 0; x < P::KLEAD; ++x)
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) st.kr[x][kc] = __builtin_bit_cast(v4i, ksrc(x)[kc * 64 + lane]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int x = 0; x < P::VLEAD; ++x)
 #pragma unroll
     for (int a = 0; a < VQ; ++a) st.vr[x][a] = __builtin_bit_cast(v4u, vsrc(x)[a * 64 + lane]);
+  __builtin_amdgcn_sched_barrier(0);
   // quarters -2, -1 meet zero probabilities: make them finite
 #pragma unroll
   for (int a = 0; a < VQ; ++a) {
@@ -406,21 +411,32 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     st.s[0][u] = acc;
   }
 
+  // Per-block scalars run ahead of their use so that no scalar load is waited
+  // for inside an iteration: kept entries two iterations ahead, logit scales
+  // one iteration ahead.  jb[e] = kept entry of block 2 it + e (e < 4, the
+  // last one for blocks past the list), cb[e] = its logit scale (e < 2).
+  static_assert(P::KLEAD <= 8 && P::VLEAD <= 8, "load sources reach at most four blocks ahead");
+  auto kle = [&](int n) { return kl[n < kb ? n : kb - 1]; };
+  int jb[4] = {kle(0), kle(1), kle(2), kle(3)};
+  float cb[2] = {dqi * dk[headblk + jb[0]], dqi * dk[headblk + jb[1]]};
   const int iters = (kb + 1) >> 1;
   for (int it = 0; it < iters; ++it) {
+    // issued here, first read at the end of the iteration
+    const int jn4 = kle(2 * it + 4), jn5 = kle(2 * it + 5);
+    const float dk2 = dk[headblk + jb[2]], dk3 = dk[headblk + jb[3]];
     PipeBlocks pb;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int n = 2 * it + e;
-      const bool valid = n < kb;
-      const float c = dqi * dk[headblk + kl[valid ? n : kb - 1]];
-      pb.c[e] = c;
+      const bool valid = 2 * it + e < kb;
+      pb.c[e] = cb[e];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pb.nm[e][u] = valid ? -__builtin_fmaf(SCORE_BIAS, c, m[u]) : -INFINITY;
+      for (int u = 0; u < 4; ++u) pb.nm[e][u] = valid ? -__builtin_fmaf(SCORE_BIAS, cb[e], m[u]) : -INFINITY;
     }
-    const int sig = 8 * it;
+    // K tile / V quarter x = 8 it + R + LEAD lies in block 2 it + (R + LEAD) / 4
+#define SLA_SRC(base, FR, PER, R, LEAD) \
+    ((base) + ((headblk + jb[((R) + (LEAD)) >> 2]) * (FR) + (((R) + (LEAD)) & 3) * (PER)) * 64)
 #define SLA_SUB(R) \
-    sub_stage<D, R>(st, qf, pb, ksrc(sig + R + P::KLEAD), vsrc(sig + R + P::VLEAD), lane)
+    sub_stage<D, R>(st, qf, pb, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
     SLA_SUB(0);
     SLA_SUB(1);
     SLA_SUB(2);
@@ -430,6 +446,13 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     SLA_SUB(6);
     SLA_SUB(7);
 #undef SLA_SUB
+#undef SLA_SRC
+    jb[0] = jb[2];
+    jb[1] = jb[3];
+    jb[2] = jn4;
+    jb[3] = jn5;
+    cb[0] = dqi * dk2;
+    cb[1] = dqi * dk3;
   }
   // drain: PV of the last chunk (parity 1) with V quarters in slots 6 and 7
   {
