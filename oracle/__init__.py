@@ -245,10 +245,12 @@ def head_prep(Q, K, topk_frac, smooth=True) -> HeadPrep:
 
 
 def head_forward(Q, K, V, W, topk_frac, use_linear=True, sm_scale=None, blocks=None,
-                 prep: HeadPrep | None = None, states=None, smooth=True, parts=False):
+                 prep: HeadPrep | None = None, states=None, smooth=True, parts=False,
+                 qk_int8=True):
     """SageSLA forward of one head in float64 for the query blocks ``blocks``
     (all by default).  Returns {i: out[n_i, d]} (and the two branches when
-    ``parts``)."""
+    ``parts``).  ``qk_int8=False`` is plain SLA: the same selection and linear
+    branch, the exact branch's logits from the bf16 inputs themselves."""
     Q, K, V = _u16(Q), _u16(K), _u16(V)
     N, d = Q.shape
     T = nblocks(N)
@@ -260,7 +262,10 @@ def head_forward(Q, K, V, W, topk_frac, use_linear=True, sm_scale=None, blocks=N
         states = linear_states(K, V)
     res = {}
     for i in (range(T) if blocks is None else blocks):
-        Os = sparse_block(i, prep.kept[i], Q, K, V, sm_scale, prep.q8, prep.dq, prep.k8, prep.dk)
+        if qk_int8:
+            Os = sparse_block(i, prep.kept[i], Q, K, V, sm_scale, prep.q8, prep.dq, prep.k8, prep.dk)
+        else:
+            Os = sparse_block(i, prep.kept[i], Q, K, V, sm_scale)
         if use_linear:
             Ol = linear_block(i, prep.mask[i], Q, states[0], states[1])
         else:

@@ -8,28 +8,27 @@
 //
 // One wave owns one 64-row query block and walks its kept key blocks in
 // ascending order:
-//   S^T = K8_j Q8_i^T          v_mfma_i32_16x16x64_i8 (exact int32)
-//   p   = exp2(S * dq_i dk_j sm_scale log2(e) - m)   online softmax, bf16 P
-//   O^T += V_j^T P^T           v_mfma_f32_16x16x32_bf16
-// The S^T accumulator puts one query and 16 keys in each lane, so the row max
-// is a register reduction plus two cross-lane steps, and a lane's
+//   S^T = K_j Q_i^T       v_mfma_i32_16x16x64_i8 on the INT8 codes (exact
+//                         int32), or v_mfma_f32_16x16x32_bf16 on bf16 Q and K
+//                         (plain SLA, QK8 = false)
+//   p   = exp2(S * c_ij - m)   c_ij = dq_i dk_j sm_scale log2(e) (INT8) or
+//                              sm_scale log2(e) (bf16); P cut to bf16
+//   O^T += V_j^T P^T      v_mfma_f32_16x16x32_bf16
+// The S^T accumulator puts one query and 16 keys in each lane, so a lane's
 // probabilities are already the B operand of the PV product (the V fragments
-// are stored in the matching key order).  The running max is only moved when
-// a tile's max exceeds it by more than 2^8, so rescaling O is rare; the final
-// O / l is unchanged by this.
+// are stored in the matching key order).  m is a per-row upper bound of the
+// logits (Cauchy-Schwarz on the operands), so no running max is kept; query
+// blocks whose bound is too loose go to a second launch (INT8: online max;
+// bf16: the rows' exact maxima first).  Row sums come from the matrix core
+// (a ones operand, zero at the padding keys of a head's ragged last block).
 // Epilogue: O_l^T = H_i^T phi(Q_i)^T / (phi(Q_i) . z_i), then
 // O^T += W O_l^T, all bf16 MFMA into the same accumulators, bf16 store.
 //
-// Memory: each wave owns 40 KiB of LDS, one K8 slot (8 KiB) and two V slots
-// (16 KiB each).  The fragments of key block n+1 are copied global -> LDS
-// (16-byte direct loads, no VGPRs) while block n is computed, so every load has
-// a whole block of work to land.  On gfx950 MFMA and VALU time add up rather
-// than overlap, so the softmax keeps its per-score work to convert, FMA, exp2,
-// half a pack and half a dot2, and padding keys are not masked per element:
-// their exactly known contribution is subtracted from the row sum.
+// Operands stream from HBM/L2 straight into registers in MFMA fragment order
+// (no LDS), through register rings several 16-key tiles ahead.
 //
-// MFMA work per kept pair (d = 128): 2*64*64*128 int8 ops + as many bf16
-// flops.
+// MFMA work per kept pair (d = 128): 2*64*64*128 int8 ops (or bf16 flops for
+// QK^T in bf16) + 2*64*64*128 bf16 flops for PV.
 #include "sla_internal.h"
 
 namespace sla {
@@ -235,7 +234,7 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
 // stream of 16-key tiles (sub-stage sigma = 4 n + t: block n, key tile t).
 // Sub-stage sigma issues three independent pieces of work, interleaved in a
 // fixed order so that vector ALU work runs while the matrix core is busy:
-//   QK(sigma+1): S^T of tile sigma+1                         (int8 MFMA)
+//   QK(sigma+1): S^T of tile sigma+1           (int8 or bf16 MFMA, by QK8)
 //   SM(sigma):   probabilities of tile sigma, half a B fragment
 //   PV:          O^T += V^T P^T for the 32-key chunk finished two
 //                sub-stages earlier, half of the channel tiles (bf16 MFMA)
@@ -247,13 +246,42 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
 // constant.
 // ---------------------------------------------------------------------------
 
-template <int D>
+// The QK^T operand types: QK8 = INT8 codes (v_mfma_i32_16x16x64_i8, exact
+// int32, biased accumulators), otherwise bf16 (v_mfma_f32_16x16x32_bf16,
+// float32 accumulators from zero).  NK = MFMAs (k chunks) per score tile.
+template <int D, bool QK8>
+struct QKOps {
+  static constexpr int NK = QK8 ? D / 64 : D / 32;
+  using frag = std::conditional_t<QK8, v4i, v4u>;  // K and Q fragments
+  using acc = std::conditional_t<QK8, v4i, v4f>;   // S^T accumulator tile
+  static __device__ __forceinline__ acc init() {
+    if constexpr (QK8) return v4i{SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
+    else return v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  static __device__ __forceinline__ acc mma(const frag &k, const frag &q, const acc &c) {
+    if constexpr (QK8) return mfma_i8(k, q, c);
+    else return mfma_bf16(k, q, c);
+  }
+  // the score as the float the exp2 argument is formed from
+  static __device__ __forceinline__ float score(const acc &s, int r) {
+    if constexpr (QK8) return __int_as_float(s[r]);
+    else return s[r];
+  }
+  // that float for a zero score, and the exp2 offset for row bound m
+  static constexpr float ZERO = QK8 ? SCORE_BIAS : 0.0f;
+  static __device__ __forceinline__ float nm(float c, float m) { return -__builtin_fmaf(ZERO, c, m); }
+};
+
+template <int D, bool QK8>
 struct Pipe {
-  static constexpr int KC = D / 64, CG = D / 16;
+  static constexpr int KC = QKOps<D, QK8>::NK, CG = D / 16;
   static constexpr int KT = KC;          // 1 KiB fragments per K tile (16 keys)
   static constexpr int VQ = CG / 2;      // 1 KiB fragments per V quarter
-  static constexpr int KLEAD = 4;        // K tile sigma + KLEAD is loaded at sub-stage sigma
-  static constexpr int VLEAD = 4;        // V quarter sigma + VLEAD is loaded at sub-stage sigma
+  // K tile sigma + KLEAD and V quarter sigma + VLEAD are loaded at sub-stage
+  // sigma; bf16 Q and K fragments take twice the registers of INT8 ones, so
+  // that path keeps shorter rings
+  static constexpr int KLEAD = QK8 ? 4 : 2;
+  static constexpr int VLEAD = QK8 ? 4 : 2;
 };
 
 // Probabilities: p = exp2(score * c + nm) cut to bf16 by keeping the upper
@@ -263,36 +291,43 @@ struct Pipe {
 // A fragment of 16 rows of bf16 ones: the rows of ones^T P^T are row sums of P.
 constexpr uint32_t BF16_ONE_PAIR = 0x3F803F80u;
 
-template <int D>
+template <int D, bool QK8>
 struct PipeState {
-  static constexpr int KC = D / 64, CG = D / 16, VQ = CG / 2;
+  using Q = QKOps<D, QK8>;
+  static constexpr int KC = Q::NK, CG = D / 16, VQ = CG / 2;
   v4f o[CG][4];
-  v4f lacc[4];        // row sums (every element of lacc[u] holds the same sum)
-  v4i s[2][4];        // S^T of the two most recent tiles (by tile parity)
-  v4u pf[2][4];       // B fragments of the two most recent 32-key chunks
-  v4i kr[8][KC];      // K tiles (by tile index mod 8)
-  v4u vr[8][VQ];      // V quarters (by quarter index mod 8)
+  v4f lacc[4];                   // row sums (every element of lacc[u] holds the same sum)
+  typename Q::acc s[2][4];       // S^T of the two most recent tiles (by tile parity)
+  v4u pf[2][4];                  // B fragments of the two most recent 32-key chunks
+  typename Q::frag kr[8][KC];    // K tiles (by tile index mod 8)
+  v4u vr[8][VQ];                 // V quarters (by quarter index mod 8)
 };
 
 // Block-level values of one loop iteration (two blocks)
 struct PipeBlocks {
   float c[2];         // logit scale of block 2i, 2i+1
-  float nm[2][4];     // -(bias * c + m_u); -inf for a block past the kept list
+  float nm[2][4];     // QKOps::nm(c, m_u); -inf for a block past the kept list
+  int last[3];        // block 2i-1, 2i, 2i+1 is the head's last (ragged) block
 };
 
 // Sub-stage R (0..7) of the loop body; sigma = 8 i + R.
-template <int D, int R>
-__device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D / 64],
-                                          const PipeBlocks &pb, const uint4 *kload_src,
-                                          const uint4 *vload_src, int lane) {
-  using P = Pipe<D>;
+// lm[h]: the ones fragment for half h of the head's last block, zero at its
+// padding keys, so the row sums leave those keys out.
+template <int D, bool QK8, int R>
+__device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
+                                          const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK],
+                                          const PipeBlocks &pb, const v4u (&lm)[2],
+                                          const uint4 *kload_src, const uint4 *vload_src,
+                                          int lane) {
+  using P = Pipe<D, QK8>;
+  using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, VQ = P::VQ;
   // loads: K tile sigma+KLEAD, V quarter sigma+VLEAD, kept together at the
   // head of the sub-stage
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
-    st.kr[(R + P::KLEAD) % 8][kc] = __builtin_bit_cast(v4i, kload_src[kc * 64 + lane]);
+    st.kr[(R + P::KLEAD) % 8][kc] = __builtin_bit_cast(typename Q::frag, kload_src[kc * 64 + lane]);
 #pragma unroll
   for (int a = 0; a < VQ; ++a)
     st.vr[(R + P::VLEAD) % 8][a] = __builtin_bit_cast(v4u, vload_src[a * 64 + lane]);
@@ -308,14 +343,19 @@ __device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D
   // sigma-2.
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    st.s[(R + 1) & 1][u] = v4i{SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
+    st.s[(R + 1) & 1][u] = Q::init();
   constexpr int blk = R / 4;
   constexpr int par = (R / 2) & 1;         // chunk being filled by SM
   constexpr int par2 = ((R / 2) + 1) & 1;  // chunk consumed by PV
   constexpr int vs = (R + 6) % 8;
   constexpr int a0 = (R & 1) * VQ;
   constexpr int NM = 4 * KC + 4 * VQ + ((R & 1) == 0 ? 4 : 0);
+  // row sums of chunk sigma/2 - 1 (even R): its block is 2i-1, 2i, 2i or
+  // 2i+1 for R = 0, 2, 4, 6, and its half within the block is R/2 + 1 mod 2
+  constexpr int cblk = R == 0 ? 0 : (R == 6 ? 2 : 1);
+  constexpr int chf = ((R / 2) + 1) & 1;
   const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
+  const v4u rs = pb.last[cblk] ? lm[chf] : ones;
   const float c = pb.c[blk];
   constexpr int NSLOT = NM > 16 ? NM : 16;  // d = 64 has fewer MFMAs than scores on odd R
   uint32_t xs[4][4];
@@ -325,20 +365,20 @@ __device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D
       // no MFMA left in this slot
     } else if (i < 4 * KC) {
       const int kc = i / 4, u = i % 4;
-      st.s[(R + 1) & 1][u] = mfma_i8(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
+      st.s[(R + 1) & 1][u] = Q::mma(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
     } else if (i < 4 * KC + 4 * VQ) {
       const int j = i - 4 * KC, a = j / 4, u = j % 4;
       st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par2][u], st.o[a0 + a][u]);
     } else {
       const int u = i - 4 * KC - 4 * VQ;
-      st.lacc[u] = mfma_bf16(ones, st.pf[par2][u], st.lacc[u]);
+      st.lacc[u] = mfma_bf16(rs, st.pf[par2][u], st.lacc[u]);
     }
     if (i < 16) {
       // p = exp2(score * c + nm), cut to bf16 by keeping the upper half of
       // the float32 (one byte permute per pair)
       const int u = i / 4, r = i % 4;
       xs[u][r] = __float_as_uint(
-          __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(st.s[R & 1][u][r]), c, pb.nm[blk][u])));
+          __builtin_amdgcn_exp2f(__builtin_fmaf(Q::score(st.s[R & 1][u], r), c, pb.nm[blk][u])));
       if (r == 3) {
         // bytes 2,3 of the first value, then bytes 2,3 of the second
         const uint32_t p0 = __builtin_amdgcn_perm(xs[u][1], xs[u][0], 0x07060302u);
@@ -356,14 +396,14 @@ __device__ __forceinline__ void sub_stage(PipeState<D> &st, const v4i (&qf)[4][D
   }
 }
 
-template <int D>
-__device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f (&o)[D / 16][4],
-                                                const float (&m)[4], float (&lsum)[4],
-                                                const int32_t *kl, int kb, const float *dk,
-                                                const uint4 *k8u, const uint4 *vtu,
-                                                size_t headblk, float dqi, int T, int npad_blk,
-                                                int lane) {
-  using P = Pipe<D>;
+// K fragments come from k8u (QK8: INT8 codes) or the bf16 copy (bfk_off).
+template <int D, bool QK8>
+__device__ __forceinline__ void kept_loop_piped(
+    const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK], v4f (&o)[D / 16][4],
+    const float (&m)[4], float (&lsum)[4], const int32_t *kl, int kb, const float *dk,
+    const uint4 *k8u, const uint4 *vtu, size_t headblk, float dqi, int T, int nlast, int lane) {
+  using P = Pipe<D, QK8>;
+  using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, CG = P::CG, VQ = P::VQ, KT = P::KT;
   constexpr int KFR = 4 * KT, VFR = 4 * VQ;  // fragments per block
   if (kb <= 0) return;
@@ -372,7 +412,27 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
   auto ksrc = [&](int x) { return k8u + ((headblk + kblk(x)) * KFR + (x & 3) * KT) * 64; };
   auto vsrc = [&](int x) { return vtu + ((headblk + kblk(x)) * VFR + (x & 3) * VQ) * 64; };
 
-  PipeState<D> st;
+  // ones fragments for the two halves of the last block, zero at its padding
+  // keys: lane group g, element e holds key 32 h + 16 (e/4) + 4 g + e%4
+  v4u lm[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int d2 = 0; d2 < 4; ++d2) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int e = 2 * d2 + b;
+        const int key = 32 * h + 16 * (e >> 2) + 4 * (lane >> 4) + (e & 3);
+        if (key < nlast) x |= 0x3F80u << (16 * b);
+      }
+      wv[d2] = x;
+    }
+    lm[h] = v4u{wv[0], wv[1], wv[2], wv[3]};
+  }
+
+  PipeState<D, QK8> st;
 #pragma unroll
   for (int a = 0; a < CG; ++a)
 #pragma unroll
@@ -389,7 +449,8 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
 #pragma unroll
   for (int x = 0; x < P::KLEAD; ++x)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) st.kr[x][kc] = __builtin_bit_cast(v4i, ksrc(x)[kc * 64 + lane]);
+    for (int kc = 0; kc < KC; ++kc)
+      st.kr[x][kc] = __builtin_bit_cast(typename Q::frag, ksrc(x)[kc * 64 + lane]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int x = 0; x < P::VLEAD; ++x)
@@ -405,9 +466,9 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
   // QK(0)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    v4i acc = {SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS, SCORE_BIAS_BITS};
+    typename Q::acc acc = Q::init();
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) acc = mfma_i8(st.kr[0][kc], qf[u][kc], acc);
+    for (int kc = 0; kc < KC; ++kc) acc = Q::mma(st.kr[0][kc], qf[u][kc], acc);
     st.s[0][u] = acc;
   }
 
@@ -418,6 +479,7 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
   static_assert(P::KLEAD <= 8 && P::VLEAD <= 8, "load sources reach at most four blocks ahead");
   auto kle = [&](int n) { return kl[n < kb ? n : kb - 1]; };
   int jb[4] = {kle(0), kle(1), kle(2), kle(3)};
+  int jprev = -1;  // kept entry of block 2 it - 1
   float cb[2] = {dqi * dk[headblk + jb[0]], dqi * dk[headblk + jb[1]]};
   const int iters = (kb + 1) >> 1;
   for (int it = 0; it < iters; ++it) {
@@ -425,18 +487,21 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     const int jn4 = kle(2 * it + 4), jn5 = kle(2 * it + 5);
     const float dk2 = dk[headblk + jb[2]], dk3 = dk[headblk + jb[3]];
     PipeBlocks pb;
+    pb.last[0] = jprev == T - 1;
+    pb.last[1] = jb[0] == T - 1;
+    pb.last[2] = jb[1] == T - 1;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const bool valid = 2 * it + e < kb;
       pb.c[e] = cb[e];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pb.nm[e][u] = valid ? -__builtin_fmaf(SCORE_BIAS, cb[e], m[u]) : -INFINITY;
+      for (int u = 0; u < 4; ++u) pb.nm[e][u] = valid ? Q::nm(cb[e], m[u]) : -INFINITY;
     }
     // K tile / V quarter x = 8 it + R + LEAD lies in block 2 it + (R + LEAD) / 4
 #define SLA_SRC(base, FR, PER, R, LEAD) \
     ((base) + ((headblk + jb[((R) + (LEAD)) >> 2]) * (FR) + (((R) + (LEAD)) & 3) * (PER)) * 64)
 #define SLA_SUB(R) \
-    sub_stage<D, R>(st, qf, pb, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
+    sub_stage<D, QK8, R>(st, qf, pb, lm, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
     SLA_SUB(0);
     SLA_SUB(1);
     SLA_SUB(2);
@@ -447,6 +512,7 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     SLA_SUB(7);
 #undef SLA_SUB
 #undef SLA_SRC
+    jprev = jb[1];
     jb[0] = jb[2];
     jb[1] = jb[3];
     jb[2] = jn4;
@@ -454,11 +520,13 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
     cb[0] = dqi * dk2;
     cb[1] = dqi * dk3;
   }
-  // drain: PV of the last chunk (parity 1) with V quarters in slots 6 and 7
+  // drain: PV of the last chunk (parity 1, half 1 of block 2 iters - 1) with
+  // V quarters in slots 6 and 7
   {
     const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
+    const v4u rs = jprev == T - 1 ? lm[1] : ones;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) st.lacc[u] = mfma_bf16(ones, st.pf[1][u], st.lacc[u]);
+    for (int u = 0; u < 4; ++u) st.lacc[u] = mfma_bf16(rs, st.pf[1][u], st.lacc[u]);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -467,38 +535,89 @@ __device__ __forceinline__ void kept_loop_piped(const v4i (&qf)[4][D / 64], v4f 
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         st.o[h * VQ + a][u] = mfma_bf16(st.vr[6 + h][a], st.pf[1][u], st.o[h * VQ + a][u]);
-  // complete row sums (every key of every kept block)
+  // complete row sums (every valid key of every kept block; padding keys of
+  // the last block met zeros in the row-sum operand, and their V rows are
+  // zero, so they add nothing anywhere)
 #pragma unroll
   for (int u = 0; u < 4; ++u) lsum[u] = st.lacc[u][0];
-  // padding keys (score 0) of the last key block: remove their share of the
-  // row sums; a kept list is ascending, so only its last entry can be T-1
-  if (kl[kb - 1] == T - 1 && npad_blk > 0) {
-    const float c = dqi * dk[headblk + T - 1];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float nm = -__builtin_fmaf(SCORE_BIAS, c, m[u]);
-      const uint32_t x0 = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(SCORE_BIAS, c, nm)));
-      lsum[u] -= (float)npad_blk * __uint_as_float(x0 & 0xFFFF0000u);
-    }
-  }
 #pragma unroll
   for (int a = 0; a < CG; ++a)
 #pragma unroll
     for (int u = 0; u < 4; ++u) o[a][u] = st.o[a][u];
 }
 
+// bf16 QK^T: Q fragments (B operands of S^T = K Q^T) straight from Q: lane
+// (query 16u + l%16, group g) holds channels 32kc + 8g .. +7 of its row.
+// Rows past N read row N-1 (their outputs are never stored).
+template <int D>
+__device__ __forceinline__ void load_qbf(const uint16_t *Qh, int i, int N, v4u (&qf)[4][D / 32],
+                                         int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = min(i * BLK + 16 * u + l16, N - 1);
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc)
+      qf[u][kc] = *(const v4u *)(Qh + (size_t)row * D + 32 * kc + 8 * g);
+  }
+}
+
+// bf16 QK^T, a query block whose bound is too loose: the exact largest logit
+// of each row (log2 units, at least 0) over the valid keys of its kept
+// blocks, for the bound loop to use in place of the bound.
+template <int D>
+__device__ void exact_row_max(const v4u (&qf)[4][D / 32], const int32_t *kl, int kb,
+                              const uint4 *kbu, size_t headblk, int T, int nlast, float c,
+                              float (&m)[4], int lane) {
+  constexpr int NK = D / 32;
+  const int g = lane >> 4;
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int n = 0; n < kb; ++n) {
+    const int j = kl[n];
+    const int nj = j == T - 1 ? nlast : BLK;
+    const uint4 *kp = kbu + (headblk + j) * (4 * NK * 64) + lane;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v4u kf[NK];
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) kf[kc] = __builtin_bit_cast(v4u, kp[(t * NK + kc) * 64]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v4f a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) a = mfma_bf16(kf[kc], qf[u][kc], a);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * t + 4 * g + r < nj) mx[u] = fmaxf(mx[u], a[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], 16, 64));
+    mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], 32, 64));
+    // at least 0: a padding key (score 0) then gets p <= 1, never an
+    // overflow (its V row is zero and it is left out of the row sums)
+    m[u] = fmaxf(mx[u] * c, 0.0f);
+  }
+}
+
 // BOUND = true: the main launch.  A query block whose logit bound exceeds
-// BOUND_LIMIT, or whose logit scale c exceeds BIAS_C_LIMIT, is only flagged
-// (flags[qb] = 1) and left to the second launch, BOUND = false, which runs the
-// online-max loop (plain int -> float scores) for flagged blocks only.
-template <int D, bool LIN, bool BOUND>
+// BOUND_LIMIT, or (INT8) whose logit scale c exceeds BIAS_C_LIMIT, is only
+// flagged (flags[qb] = 1) and left to the second launch, BOUND = false, which
+// handles flagged blocks only: INT8 with the online-max loop (plain int ->
+// float scores), bf16 with the bound loop run on the rows' exact maxima.
+// QK8 = false: QK^T in bf16 from Q itself and the bf16 copy of K in kfr (no
+// INT8 step, no scales; the logit scale is sm_scale alone).
+template <int D, bool LIN, bool BOUND, bool QK8>
 __global__ __launch_bounds__(256, 1) void k_attn(
-    const int8_t *__restrict__ q8, const int8_t *__restrict__ k8, const float *__restrict__ dq,
+    const int8_t *__restrict__ q8, const void *__restrict__ kfr, const float *__restrict__ dq,
     const float *__restrict__ dk, const float *__restrict__ dkn, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
     int32_t *__restrict__ flags, int N, int T, int kb, int nqb, int F, float qk_scale) {
-  constexpr int KC = D / 64, CG = D / 16, KC32 = D / 32;
+  constexpr int CG = D / 16, KC32 = D / 32;
+  constexpr int KC = QKOps<D, QK8>::NK;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
@@ -508,9 +627,10 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   const int g = lane >> 4, l16 = lane & 15;
   const int nlast = N - (T - 1) * BLK;
 
-  v4i qf[4][KC];
-  load_q8<D>(q8 + (size_t)qb * BLK * D, qf, lane);
-  const float dqi = dq[qb] * qk_scale;
+  typename QKOps<D, QK8>::frag qf[4][KC];
+  if constexpr (QK8) load_q8<D>(q8 + (size_t)qb * BLK * D, qf, lane);
+  else load_qbf<D>(Q + (size_t)bh * N * D, i, N, qf, lane);
+  const float dqi = QK8 ? dq[qb] * qk_scale : qk_scale;
 
   v4f o[CG][4];
 #pragma unroll
@@ -528,32 +648,52 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 #pragma unroll
     for (int r = 0; r < 4; ++r) npad_lane += (16 * t + 4 * g + r) >= nlast;
 
-  // Upper bound of the row's logits (log2 units): |q8_r . k8_s| <= ||q8_r||
-  // ||k8_s||, so logit <= dq_i sm_scale log2(e) ||q8_r|| max_j (dk_j max_s ||k8_s||).
+  // Upper bound of the row's logits (log2 units): |q_r . k_s| <= ||q_r||
+  // ||k_s||, so logit <= dq_i sm_scale log2(e) ||q_r|| max_j (dk_j max_s ||k_s||)
+  // (INT8: codes and scales; bf16: dq = dk = 1, with a margin for the float32
+  // sums of the products and norms).
   float kmax = 0.f, dkmax = 0.f;
   for (int n = 0; n < kb; ++n) {
     const int jj = kl[n];
     kmax = fmaxf(kmax, dkn[headblk + jj]);
     dkmax = fmaxf(dkmax, dk[headblk + jj]);
   }
-  bool bounded = dqi * dkmax <= BIAS_C_LIMIT;
+  bool bounded = !QK8 || dqi * dkmax <= BIAS_C_LIMIT;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    int sq = 0;
+    float qn;
+    if constexpr (QK8) {
+      int sq = 0;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t wv = (uint32_t)qf[u][kc][e];
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = (uint32_t)qf[u][kc][e];
 #pragma unroll
-        for (int b8 = 0; b8 < 4; ++b8) {
-          const int v8 = (int)(int8_t)(wv >> (8 * b8));
-          sq += v8 * v8;
+          for (int b8 = 0; b8 < 4; ++b8) {
+            const int v8 = (int)(int8_t)(wv >> (8 * b8));
+            sq += v8 * v8;
+          }
         }
-      }
-    sq += __shfl_xor(sq, 16, 64);
-    sq += __shfl_xor(sq, 32, 64);
-    m[u] = dqi * (sqrtf((float)sq) * (1.0f + 0x1p-20f)) * kmax;
+      sq += __shfl_xor(sq, 16, 64);
+      sq += __shfl_xor(sq, 32, 64);
+      qn = sqrtf((float)sq) * (1.0f + 0x1p-20f);
+    } else {
+      float sq = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = qf[u][kc][e];
+          const float lo = bf2f((uint16_t)(wv & 0xFFFF)), hi2 = bf2f((uint16_t)(wv >> 16));
+          sq = __builtin_fmaf(lo, lo, sq);
+          sq = __builtin_fmaf(hi2, hi2, sq);
+        }
+      sq += __shfl_xor(sq, 16, 64);
+      sq += __shfl_xor(sq, 32, 64);
+      qn = sqrtf(sq) * (1.0f + 0x1p-12f);
+    }
+    m[u] = dqi * qn * kmax;
     lsum[u] = 0.f;
     bounded = bounded && (m[u] <= BOUND_LIMIT);
   }
@@ -561,13 +701,17 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const bool fail = __ballot(!bounded) != 0ull;
     if (lane == 0) flags[qb] = fail ? 1 : 0;
     if (fail) return;
-    kept_loop_piped<D>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
-                       dqi, T, BLK - nlast, lane);
-  } else {
+    kept_loop_piped<D, QK8>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt,
+                            headblk, dqi, T, nlast, lane);
+  } else if constexpr (QK8) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) m[u] = -INFINITY;
-    kept_loop<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)k8, (const uint4 *)vt, headblk,
+    kept_loop<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt, headblk,
                         dqi, T, npad_lane, lane);
+  } else {
+    exact_row_max<D>(qf, kl, kb, (const uint4 *)kfr, headblk, T, nlast, dqi, m, lane);
+    kept_loop_piped<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt,
+                              headblk, dqi, T, nlast, lane);
   }
   // Row sums; O is normalised only while it is stored, so the accumulators
   // are not touched by vector ALU code in between (they stay in AGPRs).
@@ -575,7 +719,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float l = lsum[u];
-    if (!BOUND) {  // the online loop keeps per-lane partial sums
+    if (!BOUND && QK8) {  // the online loop keeps per-lane partial sums
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
     }
@@ -729,31 +873,41 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t *__restrict__ q8,
       for (int r = 0; r < 4; ++r) o[(16 * u + l16) * BLK + 16 * t + 4 * g + r] = s[t][u][r];
 }
 
-template <int D, bool LIN>
+template <int D, bool LIN, bool QK8>
 static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
                           hipStream_t st) {
   const int nqb = p.BH * p.T;
   dim3 grid((nqb + 3) / 4), block(256);
   const float qk_scale = p.sm_scale * LOG2E;
-  hipLaunchKernelGGL((k_attn<D, LIN, true>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.dkn,
-                     ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb, p.F,
-                     qk_scale);
-  hipLaunchKernelGGL((k_attn<D, LIN, false>), grid, block, 0, st, ws.q8, ws.k8, ws.dq, ws.dk, ws.dkn,
-                     ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb, p.F,
-                     qk_scale);
+  const void *kfr = QK8 ? (const void *)ws.k8 : (const void *)ws.kbf;
+  hipLaunchKernelGGL((k_attn<D, LIN, true, QK8>), grid, block, 0, st, ws.q8, kfr, ws.dq, ws.dk,
+                     ws.dkn, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb,
+                     p.F, qk_scale);
+  hipLaunchKernelGGL((k_attn<D, LIN, false, QK8>), grid, block, 0, st, ws.q8, kfr, ws.dq, ws.dk,
+                     ws.dkn, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb,
+                     p.F, qk_scale);
+}
+
+template <int D, bool QK8>
+static void launch_attn_d(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
+                          hipStream_t st) {
+  if (p.lin_on)
+    launch_attn_t<D, true, QK8>(p, q, ws, out, st);
+  else
+    launch_attn_t<D, false, QK8>(p, q, ws, out, st);
 }
 
 void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st) {
   if (p.d == 128) {
-    if (p.lin_on)
-      launch_attn_t<128, true>(p, q, ws, out, st);
+    if (p.qk_int8)
+      launch_attn_d<128, true>(p, q, ws, out, st);
     else
-      launch_attn_t<128, false>(p, q, ws, out, st);
+      launch_attn_d<128, false>(p, q, ws, out, st);
   } else {
-    if (p.lin_on)
-      launch_attn_t<64, true>(p, q, ws, out, st);
+    if (p.qk_int8)
+      launch_attn_d<64, true>(p, q, ws, out, st);
     else
-      launch_attn_t<64, false>(p, q, ws, out, st);
+      launch_attn_d<64, false>(p, q, ws, out, st);
   }
 }
 

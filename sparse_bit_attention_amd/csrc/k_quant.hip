@@ -18,8 +18,9 @@ namespace sla {
 
 // One wave per (head, block).  Lanes 0..D/4-1 own four channels of Q for all
 // 64 rows, lanes 32..32+D/4-1 the same channels of K; each lane adds its rows
-// in order (float32).  Q's values stay in registers for the quantisation.
-template <int D>
+// in order (float32).  Q's values stay in registers for the quantisation
+// (QUANT; the bf16 QK^T mode has no INT8 step).
+template <int D, bool QUANT>
 __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict__ Q,
                                                       const uint16_t *__restrict__ K, int N, int T,
                                                       int nblk, float *__restrict__ qbar,
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
       *(float4 *)(kbar + o) = mean;
     }
   }
+  if constexpr (!QUANT) return;
   // block amax of Q over lanes 0..31 (max is exact in any order)
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -221,16 +223,74 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
   }
 }
 
+// bf16 QK^T mode: one wave per (head, block): the raw K rows in bfk_off order
+// (an exact copy, padding rows zero); dkn = the largest row L2 norm of the
+// block (with ||q_r|| it bounds every score of the block); dk = 1 (the logit
+// scale is sm_scale alone).
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K, int N, int T,
+                                                  int nblk, uint16_t *__restrict__ kbf,
+                                                  float *__restrict__ dk, float *__restrict__ dkn) {
+  constexpr int LPR = D / 4;       // lanes per row
+  constexpr int RPI = 64 / LPR;    // rows per step
+  constexpr int STEPS = BLK / RPI;
+  constexpr int KC32 = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4][64 * D];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + w;
+  const bool live = blk < nblk;
+  const int bh = live ? blk / T : 0, t = live ? blk - (blk / T) * T : 0;
+  const int n = min(BLK, N - t * BLK);
+  const int c0 = 4 * (l % LPR), r0 = l / LPR;
+  const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + c0;
+
+  uint2 raw[STEPS];
+  if (n == BLK) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) raw[s] = *(const uint2 *)(K + base + (size_t)(s * RPI + r0) * D);
+  } else {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int r = s * RPI + r0;
+      raw[s] = make_uint2(0u, 0u);
+      if (live && r < n) raw[s] = *(const uint2 *)(K + base + (size_t)r * D);
+    }
+  }
+  float nmax = 0.f;  // max over rows of the squared L2 norm
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int r = s * RPI + r0;
+    const uint32_t p0 = raw[s].x, p1 = raw[s].y;  // zero for padding rows
+    const float e0 = bf2f(p0 & 0xFFFF), e1 = bf2f(p0 >> 16), e2 = bf2f(p1 & 0xFFFF), e3 = bf2f(p1 >> 16);
+    float sq = e0 * e0 + e1 * e1 + e2 * e2 + e3 * e3;
+    *(uint2 *)(&stage[w][bfk_off(r, c0, KC32)]) = make_uint2(p0, p1);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+    nmax = fmaxf(nmax, sq);
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, off, 64));
+  if (live && l == 0) {
+    dk[blk] = 1.0f;
+    dkn[blk] = sqrtf(nmax);
+  }
+  __syncthreads();
+  if (live) {
+    const uint4 *src = (const uint4 *)stage[w];
+    uint4 *dst = (uint4 *)(kbf + (size_t)blk * BLK * D);
+#pragma unroll
+    for (int it = 0; it < (BLK * D * 2) / (16 * 64); ++it) dst[it * 64 + l] = src[it * 64 + l];
+  }
+}
+
 void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, const WsPtrs &ws,
                          hipStream_t st) {
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
-  if (p.d == 128)
-    hipLaunchKernelGGL(k_pool_quant_q<128>, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar,
-                       ws.ksum, ws.kbar, ws.q8, ws.dq);
-  else
-    hipLaunchKernelGGL(k_pool_quant_q<64>, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar,
-                       ws.ksum, ws.kbar, ws.q8, ws.dq);
+  auto kern = p.d == 128 ? (p.qk_int8 ? k_pool_quant_q<128, true> : k_pool_quant_q<128, false>)
+                         : (p.qk_int8 ? k_pool_quant_q<64, true> : k_pool_quant_q<64, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar, ws.ksum, ws.kbar, ws.q8,
+                     ws.dq);
 }
 
 void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st) {
@@ -240,6 +300,13 @@ void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st) {
 void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st) {
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
+  if (!p.qk_int8) {
+    if (p.d == 128)
+      hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn);
+    else
+      hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn);
+    return;
+  }
   if (p.d == 128)
     hipLaunchKernelGGL(k_quant_k<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk,
                        ws.dkn);

@@ -33,7 +33,6 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.flags = (int32_t *)(b + p.off[R_FLAG]);
   w.maskt = (uint64_t *)(b + p.off[R_MASKT]);
   w.vt = (uint16_t *)(b + p.off[R_VT]);
-  w.qb = (uint16_t *)(b + p.off[R_QB]);
   w.kbf = (uint16_t *)(b + p.off[R_KB]);
   w.wsw = (uint16_t *)(b + p.off[R_WSW]);
   w.hb = (uint16_t *)(b + p.off[R_HB]);
@@ -79,7 +78,6 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   if (!(c.sm_scale >= 0.0f) || isinf(c.sm_scale)) return SLA_EINVAL;
   if (c.block != BLK) return SLA_EUNSUPPORTED;
   if (c.d != 64 && c.d != 128) return SLA_EUNSUPPORTED;
-  if (c.qk_int8 != 1) return SLA_EUNSUPPORTED;
   const long long T = ((long long)c.N + BLK - 1) / BLK;
   const long long BH = (long long)c.B * c.H;
   if (sla::selection_rows(c.d, (int)(T > (1 << 30) ? (1 << 30) : T)) < 1) return SLA_EUNSUPPORTED;
@@ -121,15 +119,14 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_MU] = (size_t)p.BH * p.d * 4;
   p.size[R_MASK] = bt * p.W64 * 8;
   p.size[R_KEPT] = bt * (size_t)(p.kb > 0 ? p.kb : 1) * 4;
-  p.size[R_Q8] = blk_elems;
-  p.size[R_K8] = blk_elems;
+  p.size[R_Q8] = p.qk_int8 ? blk_elems : 0;
+  p.size[R_K8] = p.qk_int8 ? blk_elems : 0;
   p.size[R_DQ] = bt * 4;
   p.size[R_DK] = bt * 4;
   p.size[R_DKN] = bt * 4;
   p.size[R_FLAG] = bt * 4;
   p.size[R_MASKT] = p.lin_on ? bt * p.W64 * 8 : 0;
   p.size[R_VT] = blk_elems * 2;
-  p.size[R_QB] = p.qk_int8 ? 0 : blk_elems * 2;
   p.size[R_KB] = p.qk_int8 ? 0 : blk_elems * 2;
   p.size[R_WSW] = p.lin_on ? (size_t)p.d * p.d * 2 : 0;
   p.size[R_HB] = p.lin_on ? bt * p.F * 2 : 0;

@@ -68,6 +68,13 @@ __host__ __device__ __forceinline__ int i8_off(int r, int c, int KC) {
   return ((((r >> 4) * KC + (c >> 6)) * 64 + (r & 15) + 16 * ((c & 63) >> 4)) << 4) + (c & 15);
 }
 
+// bf16 block [64 rows][D] as the A operand of v_mfma_f32_16x16x32_bf16 with k =
+// channel: fragment (row tile rt = r/16, chunk kc = c/32) is 1 KiB; lane
+// (r%16) + 16*((c%32)/8) holds the 8 consecutive channels.  Element offset:
+__host__ __device__ __forceinline__ int bfk_off(int r, int c, int KC32) {
+  return ((((r >> 4) * KC32 + (c >> 5)) * 64 + (r & 15) + 16 * ((c & 31) >> 3)) << 3) + (c & 7);
+}
+
 // bf16 operand whose k index runs over 64 block rows (keys), fragment order for
 // v_mfma_f32_16x16x32_bf16 with the 16 "rows" being channels: fragment
 // (kc2 = s/32, cg = c/16) is 1 KiB; lane (c%16) + 16*g holds the 8 keys

@@ -22,11 +22,11 @@ enum Region {
   R_DQ = SLA_WS_DQ,
   R_DK = SLA_WS_DK,
   R_DKN,  // f32 dk_j * max row L2 norm of the block's K8 codes   [BH][T]
+          //     (bf16 QK^T: max row L2 norm of the block's K rows)
   R_FLAG, // i32 query blocks left to the online-max attention    [BH][T]
   R_MASKT,// u64 mask words, word-major                          [BH][W64][T]
   R_VT,   // bf16 V per key block in kmaj_off order              [BH][T][64*d]
-  R_QB,   // bf16 Q per query block, fragment order (bf16 QK^T)  [BH][T][64*d]
-  R_KB,   // bf16 K per key block, fragment order (bf16 QK^T)    [BH][T][64*d]
+  R_KB,   // bf16 K per key block in bfk_off order (bf16 QK^T)    [BH][T][64*d]
   R_WSW,  // bf16 projection in wfrag_off order                  [d*d]
   R_HB,   // bf16 per key block linear state (hstate_off order)  [BH][T][F]
   R_HI,   // bf16 per query block marginal state (same order)    [BH][T][F]
@@ -49,7 +49,7 @@ struct WsPtrs {
   uint64_t *mask, *maskt;
   int32_t *kept, *flags;
   int8_t *q8, *k8;
-  uint16_t *vt, *qb, *kbf, *wsw, *hb, *hi;
+  uint16_t *vt, *kbf, *wsw, *hb, *hi;
 };
 
 WsPtrs ws_ptrs(const Plan &p, void *ws);
@@ -59,8 +59,6 @@ void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, co
 void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st);
 void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st);
 void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st);
-void launch_bf16_frags(const Plan &p, const uint16_t *q, const uint16_t *k, const WsPtrs &ws,
-                       hipStream_t st);
 void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const WsPtrs &ws,
                     hipStream_t st);
 void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st);

@@ -76,6 +76,9 @@ def plan_status(**kw):
     ({"topk": 1.0}, sla.SLA_OK),
     ({"N": 1}, sla.SLA_OK),
     ({"N": 2_000_000}, sla.SLA_EUNSUPPORTED),
+    ({"qk_int8": 0}, sla.SLA_OK),
+    ({"qk_int8": 0, "d": 128}, sla.SLA_OK),
+    ({"qk_int8": 2}, sla.SLA_EINVAL),
 ])
 def test_plan_validation(kw, status):
     assert plan_status(**kw) == status
@@ -148,3 +151,16 @@ def test_i8_unswizzle_is_a_permutation():
     assert sorted(y.ravel().tolist()) == list(range(64 * 128))
     x = np.arange(64 * 64).astype(np.int64)
     assert sorted(sla.i8_unswizzle(x, 64).ravel().tolist()) == list(range(64 * 64))
+
+
+def test_workspace_bf16_qk_mode():
+    """Plain SLA (bf16 QK^T) has no INT8 regions and a bf16 copy of K instead."""
+    B, H, N, d = 1, 40, 75600, 128
+    p8 = sla.Plan(B, H, N, d, 0.1)
+    pb = sla.Plan(B, H, N, d, 0.1, qk_int8=False)
+    assert pb.info.T == p8.info.T and pb.info.kb == p8.info.kb
+    assert pb.ws_region(0, "Q8")[1] == 0 and pb.ws_region(0, "K8")[1] == 0
+    T = pb.info.T
+    # two INT8 [BH][T][64 d] regions out, one bf16 [BH][T][64 d] region in
+    grow = pb.info.workspace_bytes - p8.info.workspace_bytes
+    assert abs(grow) <= 4 * 256

@@ -46,15 +46,15 @@ def f32(b):
     return synth.bf16_bits_to_f32(b).astype(np.float64)
 
 
-def run(wl: synth.Workload, inputs=None, sm_scale=0.0, out=None):
+def run(wl: synth.Workload, inputs=None, sm_scale=0.0, out=None, qk_int8=True):
     if inputs is None:
         inputs = synth.all_inputs(wl)
     q, k, v, w = inputs
     Q, K, V, W = dev(q), dev(k), dev(v), dev(w)
     m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear),
-                    sm_scale=sm_scale)
+                    sm_scale=sm_scale, qk_int8=qk_int8)
     say(f"[gpu] forward {wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} topk={wl.topk} "
-        f"lin={wl.use_linear} kb={m.plan.info.kb}")
+        f"lin={wl.use_linear} kb={m.plan.info.kb} qk={'int8' if qk_int8 else 'bf16'}")
     o = m(Q, K, V, W if wl.use_linear else None, out=out)
     torch.cuda.synchronize()
     return m, o, (Q, K, V, W), inputs
@@ -66,7 +66,7 @@ def unpack_mask(words, T):
     return bits.reshape(words.shape[0], -1)[:, :T]
 
 
-def check_head_prep(m, wl, b, h, Qh, Kh):
+def check_head_prep(m, wl, b, h, Qh, Kh, qk_int8=True):
     bh = b * wl.H + h
     prep = oracle.head_prep(Qh, Kh, float(np.float32(wl.topk)))
     T, kb, d = m.plan.info.T, m.plan.info.kb, wl.d
@@ -79,6 +79,9 @@ def check_head_prep(m, wl, b, h, Qh, Kh):
     assert np.array_equal(mask, prep.mask), f"mask differs in {int((mask != prep.mask).sum())} places"
     if kb:
         assert np.array_equal(m.region("KEPT")[bh].cpu().numpy(), prep.kept)
+    if not qk_int8:  # plain SLA: no INT8 step, unit key-block scales
+        assert np.all(g["DK"] == 1.0)
+        return prep
     q8 = sla.i8_unswizzle(m.region("Q8")[bh].cpu().numpy(), d).reshape(T * 64, d)
     k8 = sla.i8_unswizzle(m.region("K8")[bh].cpu().numpy(), d).reshape(T * 64, d)
     assert np.array_equal(q8, prep.q8)
@@ -88,10 +91,10 @@ def check_head_prep(m, wl, b, h, Qh, Kh):
     return prep
 
 
-def compare_blocks(o_head, wl, Qh, Kh, Vh, W, prep, blocks, sm_scale=None):
+def compare_blocks(o_head, wl, Qh, Kh, Vh, W, prep, blocks, sm_scale=None, qk_int8=True):
     res = oracle.head_forward(Qh, Kh, Vh, W, float(np.float32(wl.topk)),
                               use_linear=bool(wl.use_linear), blocks=blocks, prep=prep,
-                              sm_scale=sm_scale)
+                              sm_scale=sm_scale, qk_int8=qk_int8)
     got, ref = [], []
     for i in blocks:
         n = res[i].shape[0]
@@ -115,19 +118,19 @@ def assert_close(got, ref, label):
         assert mx == 0.0
 
 
-def full_compare(wl, sm_scale=0.0, inputs=None):
-    m, o, dv, inputs = run(wl, inputs=inputs, sm_scale=sm_scale)
+def full_compare(wl, sm_scale=0.0, inputs=None, qk_int8=True):
+    m, o, dv, inputs = run(wl, inputs=inputs, sm_scale=sm_scale, qk_int8=qk_int8)
     q, k, v, w = inputs
     out = host_u16(o)
     scale = sm_scale if sm_scale > 0 else None
     G, R = [], []
     for b, h in wl.heads():
-        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h])
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h], qk_int8=qk_int8)
         got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep,
-                                  list(range(m.plan.info.T)), sm_scale=scale)
+                                  list(range(m.plan.info.T)), sm_scale=scale, qk_int8=qk_int8)
         G.append(got)
         R.append(ref)
-    assert_close(np.concatenate(G), np.concatenate(R), wl.name)
+    assert_close(np.concatenate(G), np.concatenate(R), wl.name + ("" if qk_int8 else " (bf16 QK)"))
     return m, o, dv, inputs
 
 
@@ -219,6 +222,29 @@ def test_head_permutation_equivariance():
     assert torch.equal(o[:, perm].contiguous().view(torch.int16), o2.view(torch.int16))
 
 
+# ------------------------------------------------ plain SLA (bf16 QK^T) ---
+
+# The same small workloads with QK^T in bf16: the oracle's exact-logit mode.
+# dense-outlier-small and the sharp workloads have per-row logit bounds past
+# the limit, so their query blocks go through the exact-row-max launch.
+SMALL_BF16 = [w for w in SMALL if w.name in (
+    "tiny", "tiny-d128-ragged", "two-blocks", "one-token", "pure-linear", "all-kept-linear-on",
+    "sparse-only-b2", "dense-outlier-small", "quality-topk", "sharp-online-max",
+    "sharp-online-max-d64")]
+
+
+@pytest.mark.parametrize("wl", SMALL_BF16, ids=[w.name for w in SMALL_BF16])
+def test_sla_bf16_small_full_parity(wl):
+    full_compare(wl, qk_int8=False)
+
+
+def test_sla_bf16_debug_qk_unsupported():
+    wl = synth.Workload("qk-bf16", 1, 1, 300, 64, 0.5, seed=3)
+    m, o, dv, _ = run(wl, qk_int8=False)
+    with pytest.raises(sla.SlaError):
+        m.debug_qk_int32([(0, 0, 0)])
+
+
 # ---------------------------------------------------------------- full size ---
 
 BIG = ["wan1.3b-480p", "wan14b-480p", "wan14b-720p", "dense-outlier"]
@@ -264,3 +290,25 @@ def test_full_size_sampled_parity(name):
         for n, (_, i, j) in enumerate(pairs):
             assert np.array_equal(tiles[n], oracle.qk_int32(prep.q8, prep.k8, i, j))
     assert_close(np.concatenate(G), np.concatenate(R), name)
+
+
+@pytest.mark.parametrize("name", ["wan14b-720p"])
+def test_sla_bf16_full_size_sampled_parity(name):
+    wl = synth.WORKLOADS[name]
+    say(f"[gpu] generating {name}")
+    inputs = synth.all_inputs(wl)
+    m, o, dv, _ = run(wl, inputs=inputs, qk_int8=False)
+    mask_properties(m)
+    assert bool(torch.isfinite(o.float()).all())
+    q, k, v, w = inputs
+    out = host_u16(o)
+    T = m.plan.info.T
+    blocks = sorted({0, 1, T // 2, T - 1})
+    G, R = [], []
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h], qk_int8=False)
+        got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep, blocks,
+                                  qk_int8=False)
+        G.append(got)
+        R.append(ref)
+    assert_close(np.concatenate(G), np.concatenate(R), name + " (bf16 QK)")
