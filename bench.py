@@ -1,6 +1,7 @@
 """SageSLA forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b-720p]
+                    [--qk int8|bf16]
 
 One step = the whole forward (sla_quantize, then sla_prepare_kv and
 sla_attend) over one batch of seeded synthetic inputs already resident in
@@ -39,19 +40,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attn_work(wl, kb, T):
+def attn_work(wl, kb, T, qk_int8=True):
     """Algorithmic MFMA work of one launch of the attention kernel.
 
-    Per kept (query block, key block) pair: 2*64*64*d INT8 ops (QK^T) and
-    2*64*64*d bf16 flops (PV).  Per query block with the linear branch on:
-    2*64*d*d (H^T phi(Q)^T) + 2*64*d*d (projection) bf16 flops."""
+    Per kept (query block, key block) pair: 2*64*64*d INT8 ops (QK^T; bf16
+    flops in the plain SLA mode) and 2*64*64*d bf16 flops (PV).  Per query
+    block with the linear branch on: 2*64*d*d (H^T phi(Q)^T) + 2*64*d*d
+    (projection) bf16 flops."""
     BH = wl.B * wl.H
     pairs = BH * T * kb
-    i8 = pairs * 2 * 64 * 64 * wl.d
+    qk = pairs * 2 * 64 * 64 * wl.d
     bf = pairs * 2 * 64 * 64 * wl.d
     if wl.use_linear and kb < T:
         bf += BH * T * 4 * 64 * wl.d * wl.d
-    return i8, bf, pairs
+    if qk_int8:
+        return qk, bf, pairs
+    return 0, bf + qk, pairs
 
 
 def src_hash(path):
@@ -70,7 +74,7 @@ def traffic_entry():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, n_blocks, log_fn=log):
+def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True):
     """The oracle, single threaded, on one head of the workload: the head's
     whole selection/quantisation and linear states plus n_blocks query blocks;
     the head time is extrapolated to all T query blocks and reported as
@@ -86,7 +90,7 @@ def cpu_baseline(wl, n_blocks, log_fn=log):
     rng = np.random.default_rng(0)
     blocks = sorted(rng.choice(T, size=min(n_blocks, T), replace=False).tolist())
     oracle.head_forward(q, k, v, w, float(np.float32(wl.topk)), use_linear=bool(wl.use_linear),
-                        blocks=blocks, prep=prep, states=states)
+                        blocks=blocks, prep=prep, states=states, qk_int8=qk_int8)
     t2 = time.perf_counter()
     head_s = (t1 - t0) + (t2 - t1) * T / len(blocks)
     dense = 4.0 * wl.N * wl.N * wl.d
@@ -113,6 +117,8 @@ def main():
     ap.add_argument("--workload", default="wan14b-720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-blocks", type=int, default=360,
                     help="query blocks the CPU oracle baseline computes (0 = skip)")
+    ap.add_argument("--qk", choices=("int8", "bf16"), default="int8",
+                    help="QK^T operands: int8 (SageSLA, the default) or bf16 (plain SLA)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -151,7 +157,9 @@ def main():
     Q, K, V, W = up(q), up(k), up(v), up(w)
     del q, k, v
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
-    m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear), device=dev)
+    qk_int8 = args.qk == "int8"
+    m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear), device=dev,
+                    qk_int8=qk_int8)
     T, kb = m.plan.info.T, m.plan.info.kb
     out = torch.empty_like(Q)
     Wp = W if wl.use_linear else None
@@ -187,13 +195,14 @@ def main():
         f"attend {at_ms:.3f})")
 
     dense = 4.0 * wl.B * wl.H * wl.N * wl.N * wl.d
-    i8, bf, pairs = attn_work(wl, kb, T)
+    i8, bf, pairs = attn_work(wl, kb, T, qk_int8)
     # the MFMA roofline time of the kept-block work: int8 and bf16 share the units
-    t_roof_kept = (pairs * 2 * 64 * 64 * wl.d) / P_I8 + (pairs * 2 * 64 * 64 * wl.d) / P_BF16
+    t_roof_kept = (pairs * 2 * 64 * 64 * wl.d) / (P_I8 if qk_int8 else P_BF16) + \
+        (pairs * 2 * 64 * 64 * wl.d) / P_BF16
     t_roof_attn = i8 / P_I8 + bf / P_BF16
     blended_peak = (i8 + bf) / t_roof_attn
     achieved = (i8 + bf) / (at_ms * 1e-3)
-    traffic = traffic_entry()
+    traffic = traffic_entry() if qk_int8 else None
 
     res = {
         "metric": METRIC,
@@ -206,10 +215,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+bf16",
+        "dtype": "i8+bf16" if qk_int8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "block": 64,
-                   "topk": wl.topk, "kb": kb, "use_linear": wl.use_linear},
+                   "topk": wl.topk, "kb": kb, "use_linear": wl.use_linear,
+                   "qk": args.qk},
         "ms_per_call": ms_step,
         "stage_ms": {"sla_quantize": q_ms, "sla_prepare_kv": kv_ms, "sla_attend": at_ms},
         "pct_mfma_roofline_kept_blocks": 100.0 * t_roof_kept / (ms_step * 1e-3),
@@ -225,7 +235,7 @@ def main():
     }
     if args.cpu_blocks > 0:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks, qk_int8=qk_int8)
     print(json.dumps(res), flush=True)
 
 
