@@ -28,6 +28,11 @@
  * Steps 1-6 and the int32 products of 7 are reproduced bit for bit by the CPU
  * oracle; the rest matches it within max-abs 2e-2 and relative-L2 1e-2.
  *
+ * Plain SLA (qk_int8 = 0; the same pages' SLA without the low-bit step):
+ * steps 5-6 are skipped and step 7's logits are (Q_r . K_s) * sm_scale from
+ * the bf16 inputs (bf16 products, float32 sums); everything else is the
+ * same.  The oracle's float64 exact-logit mode is its reference.
+ *
  * Conventions
  *  - All device pointers are device memory of the current HIP device; all
  *    tensors are contiguous, 16-byte aligned.  The workspace is owned by the
@@ -67,7 +72,7 @@ typedef struct {
   float topk;          /* kept fraction of key blocks, in [0, 1] (sla_topk) */
   int32_t use_linear;  /* 1: add the projected linear branch; 0: sparse branch only */
   float sm_scale;      /* softmax scale; 0 selects float32(1/sqrt(d)) */
-  int32_t qk_int8;     /* 1: INT8 QK^T (SageSLA); 0: bf16 QK^T (plain SLA) */
+  int32_t qk_int8;     /* 1: INT8 QK^T (SageSLA); 0: bf16 QK^T (plain SLA); else EINVAL */
 } sla_config;
 
 typedef struct sla_plan_s *sla_plan_t;
@@ -85,7 +90,8 @@ sla_status sla_plan_info(sla_plan_t plan, int32_t *T, int32_t *kb, size_t *works
 
 /* Selection and quantisation (steps 1-6): block pooling, K mean, block
  * scores, top-k mask and kept lists, INT8 Q and K' with their scales, all into
- * the workspace.  q, k: bf16 [B,H,N,d]. */
+ * the workspace (plain SLA: a bf16 copy of K instead of the INT8 step).
+ * q, k: bf16 [B,H,N,d]. */
 sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
                         size_t ws_bytes, void *stream);
 
@@ -124,9 +130,10 @@ enum {
   SLA_WS_Q8 = 6,   /* int8 [B*H][T][64*d] per block, MFMA-fragment order:
                       byte (((r/16)*(d/64) + c/64)*64 + r%16 + 16*((c%64)/16))*16 + c%16
                       holds row r, channel c                                      */
-  SLA_WS_K8 = 7,   /* int8, same layout as Q8, of K - mu                          */
+  SLA_WS_K8 = 7,   /* int8, same layout as Q8, of K - mu (Q8, K8: 0 bytes when
+                      qk_int8 = 0)                                                */
   SLA_WS_DQ = 8,   /* float [B*H][T] Q block scales                               */
-  SLA_WS_DK = 9,   /* float [B*H][T] K' block scales                              */
+  SLA_WS_DK = 9,   /* float [B*H][T] K' block scales (1 when qk_int8 = 0)         */
   SLA_WS_COUNT = 10
 };
 
