@@ -62,6 +62,8 @@ def lib():
         L.sla_ref_linear_states.argtypes = [P, P, i32, i32, P, P]
         L.sla_ref_linear_block.argtypes = [P, P, P, P, i32, i32, i32, P]
         L.sla_ref_combine.argtypes = [P, P, P, i32, i32, i32, P]
+        L.sla_ref_quant_b128.argtypes = [P, i32, i32, P, P]
+        L.sla_ref_w8a8_gemm.argtypes = [P, P, P, P, i32, i32, i32, P, P]
         _lib = L
     return _lib
 
@@ -273,3 +275,32 @@ def head_forward(Q, K, V, W, topk_frac, use_linear=True, sm_scale=None, blocks=N
         O = combine(Os, Ol, W, use_linear)
         res[i] = (O, Os, Ol) if parts else O
     return res
+
+
+# ---- W8A8 linear layers --------------------------------------------------------
+
+WBLOCK = 128
+
+
+def quant_b128(X):
+    """bf16 bits [R][C] -> (int8 codes [R][C], float32 scales [ceil(R/128)][ceil(C/128)])."""
+    X = _u16(X)
+    R, C = X.shape
+    codes = np.empty((R, C), np.int8)
+    scales = np.empty(((R + WBLOCK - 1) // WBLOCK, (C + WBLOCK - 1) // WBLOCK), np.float32)
+    lib().sla_ref_quant_b128(_p(X), R, C, _p(codes), _p(scales))
+    return codes, scales
+
+
+def w8a8_gemm(xq, sx, wq, sw):
+    """Block-scaled INT8 GEMM, Y = X W^T: (float32 [M][N], bf16 bits [M][N])."""
+    xq = np.ascontiguousarray(xq, np.int8)
+    wq = np.ascontiguousarray(wq, np.int8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and K % WBLOCK == 0
+    y32 = np.empty((M, N), np.float32)
+    y = np.empty((M, N), np.uint16)
+    lib().sla_ref_w8a8_gemm(_p(xq), _p(np.ascontiguousarray(sx, np.float32)), _p(wq),
+                            _p(np.ascontiguousarray(sw, np.float32)), M, N, K, _p(y32), _p(y))
+    return y32, y

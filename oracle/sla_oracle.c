@@ -30,6 +30,9 @@
  * them bit for bit.  Steps 8-10 (softmax branch, linear branch, combine) are
  * float64.
  *
+ * The W8A8 linear-layer functions at the end (block-128 INT8 quantisation and
+ * the block-scaled GEMM) are integer / float32 exactly as written too.
+ *
  * Parity pins: see tests/test_oracle_pins.py.  Every function here is pinned.
  */
 #include <math.h>
@@ -356,5 +359,75 @@ void sla_ref_combine(const double *Os, const double *Ol, const uint16_t *W, int 
         v += p;
       }
       out[(size_t)r * d + c2] = v;
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * W8A8 linear layers ("揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化";
+ * "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写"): weights and
+ * activations both INT8, quantised over 128 x 128 blocks.  Readings: the
+ * scale recipe of step 5 per block (symmetric, amax / 127, round half to
+ * even, clamp to [-127, 127]; a block of zeros has scale 0 and zero codes);
+ * edge blocks of a matrix whose sides are not multiples of 128 are ragged.
+ * ------------------------------------------------------------------------- */
+#define SLA_REF_WB 128
+
+/* X bf16 [R][C] -> codes int8 [R][C], scales float [ceil(R/128)][ceil(C/128)]. */
+void sla_ref_quant_b128(const uint16_t *X, int R, int C, int8_t *codes, float *scales) {
+  int RB = (R + SLA_REF_WB - 1) / SLA_REF_WB, CB = (C + SLA_REF_WB - 1) / SLA_REF_WB;
+  for (int rb = 0; rb < RB; ++rb)
+    for (int cb = 0; cb < CB; ++cb) {
+      int r0 = rb * SLA_REF_WB, c0 = cb * SLA_REF_WB;
+      int r1 = r0 + SLA_REF_WB < R ? r0 + SLA_REF_WB : R;
+      int c1 = c0 + SLA_REF_WB < C ? c0 + SLA_REF_WB : C;
+      float a = 0.0f;
+      for (int r = r0; r < r1; ++r)
+        for (int c = c0; c < c1; ++c) {
+          float v = fabsf(bf16f(X[(size_t)r * C + c]));
+          if (v > a) a = v;
+        }
+      scales[(size_t)rb * CB + cb] = (float)((double)a / 127.0);
+      float inv = a > 0.0f ? (float)(127.0 / (double)a) : 0.0f;
+      for (int r = r0; r < r1; ++r)
+        for (int c = c0; c < c1; ++c) {
+          float y = rintf(bf16f(X[(size_t)r * C + c]) * inv);
+          if (y > 127.0f) y = 127.0f;
+          if (y < -127.0f) y = -127.0f;
+          codes[(size_t)r * C + c] = (int8_t)y;
+        }
+    }
+}
+
+/* Y = X W^T for X [M][K], W [N][K] (the [out][in] weight of a linear layer):
+ * y[m][n] = sum over the K blocks kb in ascending order of
+ * float32(sx[m/128][kb] * sw[n/128][kb]) * A_kb, A_kb the exact int32 dot
+ * product of the block's codes.  Reading: the block terms are accumulated in
+ * float32 from +0, one fused multiply-add per block (the plain blocked
+ * accumulation); no bias.  y32 (may be NULL) receives the float32 sums, y
+ * (may be NULL) the bf16 results rounded to nearest even.  K is a multiple of
+ * 128. */
+void sla_ref_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw, int M,
+                       int N, int K, float *y32, uint16_t *y) {
+  int KB = K / SLA_REF_WB;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      float acc = 0.0f;
+      for (int kb = 0; kb < KB; ++kb) {
+        int32_t A = 0;
+        for (int k = kb * SLA_REF_WB; k < (kb + 1) * SLA_REF_WB; ++k)
+          A += (int32_t)xq[(size_t)m * K + k] * (int32_t)wq[(size_t)n * K + k];
+        float s = sx[(size_t)(m / SLA_REF_WB) * KB + kb] * sw[(size_t)(n / SLA_REF_WB) * KB + kb];
+        acc = fmaf((float)A, s, acc);
+      }
+      if (y32) y32[(size_t)m * N + n] = acc;
+      if (y) {
+        /* bf16 nearest even: keep the upper half, round up past the midpoint
+         * or at it when the kept half is odd (finite values) */
+        uint32_t u;
+        memcpy(&u, &acc, sizeof u);
+        uint32_t hi = u >> 16, lo = u & 0xFFFFu;
+        if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1u;
+        y[(size_t)m * N + n] = (uint16_t)hi;
+      }
     }
 }

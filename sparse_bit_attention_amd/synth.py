@@ -18,7 +18,7 @@ Generator (counter based, so any slice can be drawn on its own):
   then to bfloat16 (nearest even).
 
 Tensor ids: Q = 1, K noise = 2, K per-channel offset = 3, V = 4, W = 5,
-outlier-channel pick = 6.
+outlier-channel pick = 6; linear layers (W8A8): activations = 7, weights = 8.
 """
 from __future__ import annotations
 
@@ -34,6 +34,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 TID_Q, TID_KNOISE, TID_KOFF, TID_V, TID_W, TID_OUTLIER = 1, 2, 3, 4, 5, 6
+TID_LIN_X, TID_LIN_W = 7, 8
 
 _CHUNK = 1 << 22
 
@@ -194,3 +195,31 @@ def all_inputs(wl: Workload):
             wl.seed, TID_KNOISE, per_head, e * per_head, add=offs[e * wl.d:(e + 1) * wl.d])
     v = normal_bf16(wl.seed, TID_V, n)
     return q.reshape(shape), k.reshape(shape), v.reshape(shape), proj_weight(wl)
+
+
+# ---- linear layers around attention (W8A8 GEMM inputs) ----------------------
+
+@dataclass(frozen=True)
+class LinearWorkload:
+    """Y = X W^T with X [M, K] (tokens x input features), W [N, K] ([out, in])."""
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int = 0
+    x_std: float = 1.0
+
+
+# Wan2.1-14B: model width 5120 (40 heads x 128), 720P latents 21x45x80 tokens.
+LINEAR_WORKLOADS = {
+    "wan14b-720p-qkv": LinearWorkload("wan14b-720p-qkv", 21 * 45 * 80, 3 * 5120, 5120),
+    "wan14b-720p-o": LinearWorkload("wan14b-720p-o", 21 * 45 * 80, 5120, 5120),
+    "small": LinearWorkload("small", 300, 200, 384, seed=3),
+}
+
+
+def linear_inputs(lw: LinearWorkload):
+    """bf16 bits of X [M, K] ~ N(0, x_std^2) and W [N, K] ~ N(0, 1/K)."""
+    x = normal_bf16(lw.seed, TID_LIN_X, lw.M * lw.K, std=lw.x_std).reshape(lw.M, lw.K)
+    w = normal_bf16(lw.seed, TID_LIN_W, lw.N * lw.K, std=1.0 / np.sqrt(lw.K)).reshape(lw.N, lw.K)
+    return x, w

@@ -391,3 +391,119 @@ def test_value_scaling_by_power_of_two_is_exact():
     b = oracle.head_forward(Q, K, V4, W, 0.25)
     for i in a:
         assert np.array_equal(a[i] * 4.0, b[i])
+
+
+# ---- W8A8 linear layers (block-128 INT8) --------------------------------------
+
+def _bf16(x):
+    return synth.f64_to_bf16_bits(np.asarray(x, np.float64))
+
+
+def test_w8a8_quant_hand_case():
+    case = GOLD["w8a8_quant"]
+    codes, scales = oracle.quant_b128(_bf16(case["x"]))
+    assert codes.tolist() == case["codes"]
+    assert scales.shape == (1, 1)
+    assert scales[0, 0] == np.float32(case["scale_num"] / case["scale_den"])
+
+
+@pytest.mark.parametrize("R,C", [(130, 260), (128, 128), (1, 384), (257, 16)])
+def test_w8a8_quant_blocks_and_bound(R, C):
+    rng = np.random.default_rng(R * 1000 + C)
+    x = rng.standard_normal((R, C)) * rng.uniform(0.1, 10.0, size=(R, 1))
+    xb = _bf16(x)
+    xf = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    codes, scales = oracle.quant_b128(xb)
+    RB, CB = -(-R // 128), -(-C // 128)
+    assert scales.shape == (RB, CB)
+    for rb in range(RB):
+        for cb in range(CB):
+            blk = xf[rb * 128:(rb + 1) * 128, cb * 128:(cb + 1) * 128]
+            amax = np.abs(blk).max()
+            # one scale per block, from that block alone
+            assert scales[rb, cb] == np.float32(amax / 127.0)
+            q = codes[rb * 128:(rb + 1) * 128, cb * 128:(cb + 1) * 128].astype(np.float64)
+            assert np.abs(q).max() <= 127
+            # reconstruction within half a step (plus the float32 rounding of 127/amax)
+            err = np.abs(q * float(scales[rb, cb]) - blk)
+            assert err.max() <= 0.5 * float(scales[rb, cb]) * (1 + 2 ** -12)
+
+
+def test_w8a8_quant_zero_block():
+    x = np.zeros((3, 200))
+    x[:, 150] = 1.0  # only the second column block is non-zero
+    codes, scales = oracle.quant_b128(_bf16(x))
+    assert scales[0, 0] == 0.0 and np.all(codes[:, :128] == 0)
+    assert scales[0, 1] == np.float32(1.0 / 127.0) and np.all(codes[:, 150] == 127)
+
+
+def test_w8a8_gemm_hand_case():
+    K = 256
+    xq = np.zeros((1, K), np.int8)
+    xq[0, :128], xq[0, 128:] = 1, 2
+    wq = np.zeros((1, K), np.int8)
+    wq[0, :128], wq[0, 128:] = 3, -1
+    y32, y = oracle.w8a8_gemm(xq, np.array([[0.5, 0.25]], np.float32), wq,
+                              np.array([[2.0, 4.0]], np.float32))
+    assert y32[0, 0] == GOLD["w8a8_gemm"]["y"]
+    assert synth.bf16_bits_to_f32(y)[0, 0] == GOLD["w8a8_gemm"]["y"]
+
+
+def test_w8a8_gemm_unit_scales_is_integer_matmul():
+    rng = np.random.default_rng(5)
+    M, N, K = 70, 45, 384  # not square: a transposed operand would fail
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    ones_x = np.ones((1, K // 128), np.float32)
+    ones_w = np.ones((1, K // 128), np.float32)
+    y32, _ = oracle.w8a8_gemm(xq, ones_x, wq, ones_w)
+    ref = xq.astype(np.int64) @ wq.astype(np.int64).T  # |ref| < 2^24: exact in float32
+    assert np.array_equal(y32.astype(np.int64), ref)
+
+
+def _rne_bf16_reference(v32):
+    """float32 -> bf16 bits, nearest even, by comparing the two neighbouring
+    bf16 values in float64 (independent of bit tricks)."""
+    v = np.asarray(v32, np.float32)
+    lo = (v.view(np.uint32) >> np.uint32(16)).astype(np.uint32)
+    hi = lo + np.uint32(1)
+    f = lambda b: (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    d_lo = np.abs(v.astype(np.float64) - f(lo))
+    d_hi = np.abs(f(hi) - v.astype(np.float64))
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & np.uint32(1)) == 1))
+    return np.where(pick_hi, hi, lo).astype(np.uint16)
+
+
+def test_w8a8_gemm_matches_float64_and_quantisation_bound():
+    lw = synth.LINEAR_WORKLOADS["small"]
+    x, w = synth.linear_inputs(lw)
+    xq, sx = oracle.quant_b128(x)
+    wq, sw = oracle.quant_b128(w)
+    y32, y = oracle.w8a8_gemm(xq, sx, wq, sw)
+    M, K = xq.shape
+    N = wq.shape[0]
+    KB = K // 128
+    # float64 value of the same block sum
+    exact = np.zeros((M, N))
+    bound = np.zeros((M, N))
+    for kb in range(KB):
+        sl = slice(kb * 128, (kb + 1) * 128)
+        A = xq[:, sl].astype(np.int64) @ wq[:, sl].astype(np.int64).T
+        s = (np.repeat(sx[:, kb], 128)[:M, None].astype(np.float32) *
+             np.repeat(sw[:, kb], 128)[None, :N].astype(np.float32)).astype(np.float64)
+        exact += A * s
+        bound += np.abs(A * s)
+    # float32 blocked accumulation: KB fused steps, each one rounding
+    assert np.all(np.abs(y32 - exact) <= KB * 2.0 ** -24 * bound + 1e-30)
+    # bf16 output = nearest-even rounding of the float32 sum
+    assert np.array_equal(y, _rne_bf16_reference(y32))
+    # against the unquantised product: |dx| <= sx/2, |dw| <= sw/2 per element
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    dxm = np.repeat(np.repeat(sx, 128, 0), 128, 1)[:M, :K].astype(np.float64) / 2 * (1 + 2 ** -12)
+    dwm = np.repeat(np.repeat(sw, 128, 0), 128, 1)[:N, :K].astype(np.float64) / 2 * (1 + 2 ** -12)
+    qbound = np.abs(xf) @ dwm.T + dxm @ np.abs(wf).T + dxm @ dwm.T
+    ref = xf @ wf.T
+    assert np.all(np.abs(y32 - ref) <= qbound + KB * 2.0 ** -24 * bound + 1e-12)
+    # and the quantisation error is a small fraction of the signal
+    assert np.linalg.norm(y32 - ref) / np.linalg.norm(ref) < 2e-2
