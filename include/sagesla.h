@@ -147,6 +147,37 @@ sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr,
 sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *dev_pairs, int32_t n,
                               int32_t *dev_out, void *stream);
 
+/* ---- W8A8 linear layers ------------------------------------------------------
+ * Pages: "揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化" and
+ * "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写": the linear layers
+ * around attention (QKV and output projections) run with weights and
+ * activations both INT8, quantised over 128 x 128 blocks.  Readings: the step-5
+ * recipe per block (symmetric, scale = amax / 127, codes = round half to even
+ * of x * float32(127 / amax), clamped to [-127, 127]; an all-zero block has
+ * scale 0); ragged edge blocks; no bias.  Reproduced bit for bit by the CPU
+ * oracle (codes, scales and the bf16 outputs). */
+
+/* Block-128 INT8 quantisation of a bf16 matrix.
+ * x: bf16 [rows][cols] row-major; codes: int8 [rows][cols] row-major (same
+ * shape); scales: float32 [ceil(rows/128)][ceil(cols/128)].  All device
+ * memory owned by the caller; x and codes 16-byte aligned.  cols must be a
+ * multiple of 16 and ceil(rows/128) <= 65535 (else SLA_EUNSUPPORTED);
+ * rows, cols >= 1 (else SLA_EINVAL).  Asynchronous on stream. */
+sla_status sla_quant_b128(const void *x, int32_t rows, int32_t cols, void *codes, float *scales,
+                          void *stream);
+
+/* Block-scaled INT8 GEMM, y = X W^T: xq int8 [M][K] with scales sx
+ * [ceil(M/128)][K/128] (activations), wq int8 [N][K] with scales sw
+ * [ceil(N/128)][K/128] (the [out][in] weight), as sla_quant_b128 writes them;
+ * y bf16 [M][N] row-major.  y[m][n] is the float32 sum, over the K blocks kb
+ * in ascending order and from +0, of one fused multiply-add each:
+ * float32(sx[m/128][kb] * sw[n/128][kb]) times the exact int32 block dot
+ * product; then rounded to bf16 (nearest even).  K must be a multiple of 128
+ * (else SLA_EUNSUPPORTED); M, N, K >= 1 (else SLA_EINVAL); xq, wq 16-byte
+ * aligned.  Asynchronous on stream. */
+sla_status sla_w8a8_gemm(const void *xq, const float *sx, const void *wq, const float *sw,
+                         int32_t M, int32_t N, int32_t K, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

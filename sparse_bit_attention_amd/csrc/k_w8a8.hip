@@ -1,0 +1,206 @@
+// W8A8 linear layers: block-128 INT8 quantisation and the block-scaled INT8
+// GEMM Y = X W^T.
+//
+// Pages: "揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化" (weights and
+// activations of the linear layers both INT8, quantised over 128 x 128
+// blocks) and "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写" (the same,
+// run on the INT8 matrix units).
+//
+// k_quant_b128: one workgroup per 128 x 128 block of a bf16 [R][C] matrix:
+//   scale = amax / 127 (float64 division), codes = rint(x * float32(127 /
+//   amax)) clamped to [-127, 127] (round half to even); row-major int8 codes.
+// k_w8a8_gemm: a workgroup computes a 128 x 256 tile of Y with 8 waves (two
+//   per SIMD) of 64 x 64; per K block of 128 the exact int32 products come
+//   from v_mfma_i32_16x16x64_i8 and are folded into float32 accumulators with
+//   one fma by the block's scale product sx * sw (float32), blocks in
+//   ascending order.  X and W tiles pass through LDS (double-buffered, rows
+//   padded to 144 bytes so the fragment reads spread over all banks).
+//
+// On gfx950 the fold costs two vector ALU instructions per output element per
+// K block (convert, fma): as much issue time as the block's MFMAs, so the
+// kernel relies on its two waves per SIMD to overlap the two.
+#include "sla_internal.h"
+
+namespace sla {
+
+constexpr int WB = 128;  // quantisation block
+
+__global__ __launch_bounds__(256) void k_quant_b128(const uint16_t *__restrict__ X, int R, int C,
+                                                    int8_t *__restrict__ codes,
+                                                    float *__restrict__ scales) {
+  __shared__ float wmax[4];
+  const int cb = blockIdx.x, rb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = rb * WB + (tid >> 1);
+  const int c0 = cb * WB + 64 * (tid & 1);
+  const bool rok = r < R;
+  // 64 columns per thread as eight 16-byte pieces (C is a multiple of 16, so
+  // a piece is entirely inside or outside the matrix)
+  uint4 raw[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int c = c0 + 8 * p;
+    raw[p] = (rok && c < C) ? *(const uint4 *)(X + (size_t)r * C + c) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t v[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a = fmaxf(a, fmaxf(fabsf(bf2f((uint16_t)(v[e] & 0xFFFF))), fabsf(bf2f((uint16_t)(v[e] >> 16)))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  if (lane == 0) wmax[w] = a;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+  if (tid == 0) scales[(size_t)rb * gridDim.x + cb] = (float)((double)amax / 127.0);
+  if (!rok) return;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // 16 codes per store
+    const int c = c0 + 16 * p;
+    if (c >= C) break;
+    uint32_t out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v4 = raw[2 * p + (q >> 1)];
+      const uint32_t pair0 = (q & 1) ? v4.z : v4.x, pair1 = (q & 1) ? v4.w : v4.y;
+      const float x[4] = {bf2f((uint16_t)(pair0 & 0xFFFF)), bf2f((uint16_t)(pair0 >> 16)),
+                          bf2f((uint16_t)(pair1 & 0xFFFF)), bf2f((uint16_t)(pair1 >> 16))};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = __builtin_rintf(x[e] * inv);
+        y = fminf(fmaxf(y, -127.f), 127.f);
+        packed |= ((uint32_t)(uint8_t)(int8_t)(int)y) << (8 * e);
+      }
+      out[q] = packed;
+    }
+    *(uint4 *)(codes + (size_t)r * C + c) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+constexpr int GM_BM = 128, GM_BN = 256, GM_BK = 128;
+constexpr int GM_G = 16;              // row tiles per ordering group
+constexpr int GM_PITCH = GM_BK + 16;  // bytes per LDS row
+
+__global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__ xq,
+                                                      const float *__restrict__ sx,
+                                                      const int8_t *__restrict__ wq,
+                                                      const float *__restrict__ sw, int M, int N,
+                                                      int K, uint16_t *__restrict__ y) {
+  // two stages of [A 128 rows | B 256 rows] x 144 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(GM_BM + GM_BN) * GM_PITCH];
+  // Tile order: groups of GM_G row tiles; inside a group the row tile runs
+  // fastest, so consecutive workgroups (one XCD, xcd_remap) share a W tile
+  // and a group's X tiles are reused across all column tiles.
+  const int MT = (M + GM_BM - 1) / GM_BM, NT = (N + GM_BN - 1) / GM_BN;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = bid / (GM_G * NT), rem = bid - grp * (GM_G * NT);
+  const int gs = min(GM_G, MT - grp * GM_G);
+  const int tn = rem / gs, tm = grp * GM_G + (rem - tn * gs);
+  const int m0 = tm * GM_BM, n0 = tn * GM_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w >> 2, wc = w & 3;  // wave tile rows 64 wr.., columns 64 wc..
+  const int KB = K / GM_BK;
+  const int mb = m0 / WB;             // one X scale row per workgroup
+  // one W scale row per wave (clamped: a wave wholly past N stores nothing)
+  const int nb = min((n0 + 64 * wc) / WB, (N - 1) / WB);
+
+  // global -> LDS staging: 384 rows x 8 pieces of 16 bytes, 6 per thread;
+  // piece q = it * 512 + tid: row q / 8 (A rows first), piece q % 8.  Rows
+  // past M / N read the last row (never stored).
+  uint4 stg[6];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int it = 0; it < 6; ++it) {
+      const int q = it * 512 + tid, row = q >> 3, pc = q & 7;
+      const int8_t *src = row < GM_BM ? xq + (size_t)min(m0 + row, M - 1) * K
+                                      : wq + (size_t)min(n0 + row - GM_BM, N - 1) * K;
+      stg[it] = *(const uint4 *)(src + (size_t)kb * GM_BK + 16 * pc);
+    }
+  };
+  auto lstore = [&](int s) {
+#pragma unroll
+    for (int it = 0; it < 6; ++it) {
+      const int q = it * 512 + tid, row = q >> 3, pc = q & 7;
+      *(uint4 *)(&lds[s][row * GM_PITCH + 16 * pc]) = stg[it];
+    }
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const int s = kb & 1;
+    if (kb + 1 < KB) gload(kb + 1);
+    // exact int32 block products: lane (row 16 i + l%16, group g) reads
+    // bytes 64 kc + 16 g .. +15 of its row
+    v4i ia[4][4];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      v4i af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *(const v4i *)(&lds[s][(64 * wr + 16 * i + (lane & 15)) * GM_PITCH + 64 * kc + 16 * (lane >> 4)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *(const v4i *)(&lds[s][(GM_BM + 64 * wc + 16 * j + (lane & 15)) * GM_PITCH + 64 * kc +
+                                       16 * (lane >> 4)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ia[i][j] = mfma_i8(af[i], bf[j], kc == 0 ? v4i{0, 0, 0, 0} : ia[i][j]);
+    }
+    // fold the block into the float32 sums: one fma by sx * sw per element
+    const float sc = sx[(size_t)mb * KB + kb] * sw[(size_t)nb * KB + kb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf((float)ia[i][j][r], sc, acc[i][j][r]);
+    if (kb + 1 < KB) lstore(s ^ 1);
+    __syncthreads();
+  }
+  // store bf16: lane holds rows 4 (l/16) + r of column l%16 of each 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wc + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const int m = m0 + 64 * wr + 16 * i + 4 * (lane >> 4) + r;
+        const uint32_t pr = pack2bf(acc[i][j][r], acc[i][j][r + 1]);
+        if (n < N) {
+          if (m < M) y[(size_t)m * N + n] = (uint16_t)pr;
+          if (m + 1 < M) y[(size_t)(m + 1) * N + n] = (uint16_t)(pr >> 16);
+        }
+      }
+    }
+}
+
+void launch_quant_b128(const uint16_t *x, int R, int C, int8_t *codes, float *scales,
+                       hipStream_t st) {
+  dim3 grid((C + WB - 1) / WB, (R + WB - 1) / WB), block(256);
+  hipLaunchKernelGGL(k_quant_b128, grid, block, 0, st, x, R, C, codes, scales);
+}
+
+void launch_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw, int M,
+                      int N, int K, uint16_t *y, hipStream_t st) {
+  const int tiles = ((M + GM_BM - 1) / GM_BM) * ((N + GM_BN - 1) / GM_BN);
+  hipLaunchKernelGGL(k_w8a8_gemm, dim3(tiles), dim3(512), 0, st, xq, sx, wq, sw, M, N, K, y);
+}
+
+}  // namespace sla

@@ -252,4 +252,32 @@ sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *de
   return launched();
 }
 
+// ---- W8A8 linear layers ------------------------------------------------------
+
+sla_status sla_quant_b128(const void *x, int32_t rows, int32_t cols, void *codes, float *scales,
+                          void *stream) {
+  if (!x || !codes || !scales) return SLA_EINVAL;
+  if (rows < 1 || cols < 1) return SLA_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return SLA_EINVAL;
+  if (cols % 16 != 0 || (rows + 127) / 128 > 65535) return SLA_EUNSUPPORTED;
+  (void)hipGetLastError();
+  launch_quant_b128((const uint16_t *)x, rows, cols, (int8_t *)codes, scales, (hipStream_t)stream);
+  return launched();
+}
+
+sla_status sla_w8a8_gemm(const void *xq, const float *sx, const void *wq, const float *sw,
+                         int32_t M, int32_t N, int32_t K, void *y, void *stream) {
+  if (!xq || !sx || !wq || !sw || !y) return SLA_EINVAL;
+  if (M < 1 || N < 1 || K < 1) return SLA_EINVAL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 2) || !aligned(sx, 4) || !aligned(sw, 4))
+    return SLA_EINVAL;
+  if (K % 128 != 0) return SLA_EUNSUPPORTED;
+  const long long tiles = (long long)((M + 127) / 128) * ((N + 255) / 256);
+  if (tiles >= (1LL << 31)) return SLA_EUNSUPPORTED;
+  (void)hipGetLastError();
+  launch_w8a8_gemm((const int8_t *)xq, sx, (const int8_t *)wq, sw, M, N, K, (uint16_t *)y,
+                   (hipStream_t)stream);
+  return launched();
+}
+
 }  // extern "C"

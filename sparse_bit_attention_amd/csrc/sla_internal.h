@@ -66,5 +66,9 @@ void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st);
 void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st);
 void launch_debug_qk(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n, int32_t *out,
                      hipStream_t st);
+void launch_quant_b128(const uint16_t *x, int R, int C, int8_t *codes, float *scales,
+                       hipStream_t st);
+void launch_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw, int M,
+                      int N, int K, uint16_t *y, hipStream_t st);
 
 }  // namespace sla

@@ -18,7 +18,7 @@ WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "D
 
 EXPORTS = ["sla_plan", "sla_plan_destroy", "sla_plan_info", "sla_quantize", "sla_attention_fwd",
            "sla_prepare_kv", "sla_attend", "sla_status_string", "sla_ws_view",
-           "sla_debug_qk_int32"]
+           "sla_debug_qk_int32", "sla_quant_b128", "sla_w8a8_gemm"]
 
 
 class SlaError(RuntimeError):
@@ -65,6 +65,10 @@ def lib():
         L.sla_ws_view.restype = ctypes.c_int
         L.sla_debug_qk_int32.argtypes = [P, P, P, i32, P, P]
         L.sla_debug_qk_int32.restype = ctypes.c_int
+        L.sla_quant_b128.argtypes = [P, i32, i32, P, P, P]
+        L.sla_quant_b128.restype = ctypes.c_int
+        L.sla_w8a8_gemm.argtypes = [P, P, P, P, i32, i32, i32, P, P]
+        L.sla_w8a8_gemm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -229,3 +233,41 @@ def i8_unswizzle(tiles, d):
     KC = d // 64
     off = ((((r >> 4) * KC + (c >> 6)) * 64 + (r & 15) + 16 * ((c & 63) >> 4)) << 4) + (c & 15)
     return np.asarray(tiles)[..., off]
+
+
+# ---- W8A8 linear layers (see sagesla.h) ----------------------------------------
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def quant_b128(x, stream=None):
+    """bf16 [R, C] (cuda) -> (int8 codes [R, C], float32 scales [ceil(R/128), ceil(C/128)])."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    R, C = x.shape
+    codes = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    scales = torch.empty(((R + 127) // 128, (C + 127) // 128), dtype=torch.float32, device=x.device)
+    _check(lib().sla_quant_b128(ctypes.c_void_p(x.data_ptr()), R, C,
+                                ctypes.c_void_p(codes.data_ptr()),
+                                ctypes.c_void_p(scales.data_ptr()), _stream_handle(stream)),
+           "sla_quant_b128")
+    return codes, scales
+
+
+def w8a8_gemm(xq, sx, wq, sw, out=None, stream=None):
+    """Block-scaled INT8 GEMM: bf16 [M, N] = dequant(xq) dequant(wq)^T."""
+    import torch
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and xq.dtype == torch.int8 and wq.dtype == torch.int8
+    assert xq.is_contiguous() and wq.is_contiguous() and sx.is_contiguous() and sw.is_contiguous()
+    assert sx.shape == ((M + 127) // 128, K // 128) and sw.shape == ((N + 127) // 128, K // 128)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(lib().sla_w8a8_gemm(ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()),
+                               ctypes.c_void_p(wq.data_ptr()), ctypes.c_void_p(sw.data_ptr()),
+                               M, N, K, ctypes.c_void_p(y.data_ptr()), _stream_handle(stream)),
+           "sla_w8a8_gemm")
+    return y

@@ -164,3 +164,17 @@ def test_workspace_bf16_qk_mode():
     # two INT8 [BH][T][64 d] regions out, one bf16 [BH][T][64 d] region in
     grow = pb.info.workspace_bytes - p8.info.workspace_bytes
     assert abs(grow) <= 4 * 256
+
+
+def test_w8a8_argument_checks_without_gpu():
+    """Host-side validation returns before any launch, so fake aligned
+    addresses are safe here."""
+    L = sla.lib()
+    a = 1 << 20  # 16-byte aligned, never dereferenced
+    assert L.sla_w8a8_gemm(None, a, a, a, 4, 4, 128, a, None) == sla.SLA_EINVAL
+    assert L.sla_w8a8_gemm(a, a, a, a, 0, 4, 128, a, None) == sla.SLA_EINVAL
+    assert L.sla_w8a8_gemm(a, a, a, a, 4, 4, 100, a, None) == sla.SLA_EUNSUPPORTED
+    assert L.sla_w8a8_gemm(a + 8, a, a, a, 4, 4, 128, a, None) == sla.SLA_EINVAL
+    assert L.sla_quant_b128(a, 4, 20, a, a, None) == sla.SLA_EUNSUPPORTED
+    assert L.sla_quant_b128(a, 0, 16, a, a, None) == sla.SLA_EINVAL
+    assert L.sla_quant_b128(None, 4, 16, a, a, None) == sla.SLA_EINVAL

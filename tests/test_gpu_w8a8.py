@@ -1,0 +1,117 @@
+"""GPU parity of the W8A8 linear-layer kernels (block-128 INT8 quantisation and
+the block-scaled INT8 GEMM) against the CPU oracle, through the C ABI.
+
+Everything is bit-exact: codes, scales and the bf16 outputs (the GEMM's
+float32 blocked accumulation is part of the definition).  Small and ragged
+shapes are compared in full; the Wan-14B-720P QKV projection runs at full
+size and is compared on sampled row and column blocks (first, middle, last).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_bit_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_bit_attention_amd import sla  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_linear(x, w):
+    X, W = dev(x), dev(w)
+    xq, sx = sla.quant_b128(X)
+    wq, sw = sla.quant_b128(W)
+    y = sla.w8a8_gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    return xq, sx, wq, sw, y
+
+
+SHAPES = [
+    synth.LinearWorkload("small", 300, 200, 384, seed=3),
+    synth.LinearWorkload("one-by-one", 1, 1, 128, seed=4),
+    synth.LinearWorkload("ragged", 129, 257, 256, seed=5),
+    synth.LinearWorkload("wide", 64, 1000, 512, seed=6, x_std=30.0),
+    synth.LinearWorkload("tall", 700, 48, 1024, seed=7, x_std=0.01),
+]
+
+
+@pytest.mark.parametrize("lw", SHAPES, ids=[s.name for s in SHAPES])
+def test_w8a8_full_parity(lw):
+    say(f"[gpu] w8a8 {lw.name} M={lw.M} N={lw.N} K={lw.K}")
+    x, w = synth.linear_inputs(lw)
+    xq, sx, wq, sw, y = gpu_linear(x, w)
+    rxq, rsx = oracle.quant_b128(x)
+    rwq, rsw = oracle.quant_b128(w)
+    assert np.array_equal(xq.cpu().numpy(), rxq)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), rsx.view(np.uint32))
+    assert np.array_equal(wq.cpu().numpy(), rwq)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), rsw.view(np.uint32))
+    _, ry = oracle.w8a8_gemm(rxq, rsx, rwq, rsw)
+    got = host_u16(y)
+    nbad = int((got != ry).sum())
+    say(f"[parity] w8a8 {lw.name}: {nbad} of {got.size} outputs differ")
+    assert nbad == 0
+
+
+def test_w8a8_quant_ragged_columns_and_zero_block():
+    R, C = 200, 144  # a 16-column tail block
+    x = np.zeros((R, C), np.float64)
+    x[130:, 20:] = np.linspace(-3, 5, (R - 130) * (C - 20)).reshape(R - 130, C - 20)
+    xb = synth.f64_to_bf16_bits(x)
+    codes, scales = sla.quant_b128(dev(xb))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant_b128(xb)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert rs[0, 0] == 0.0 and rs[0, 1] == 0.0  # the top row blocks are all zero
+
+
+def test_w8a8_rejects_bad_k():
+    xq = torch.zeros((4, 100), dtype=torch.int8, device="cuda")
+    sx = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+    # the binding asserts shapes; call the C entry point directly
+    st = sla.lib().sla_w8a8_gemm(xq.data_ptr(), sx.data_ptr(), xq.data_ptr(), sx.data_ptr(),
+                                 4, 4, 100, xq.data_ptr(), None)
+    assert st == sla.SLA_EUNSUPPORTED
+
+
+def test_w8a8_full_size_sampled():
+    lw = synth.LINEAR_WORKLOADS["wan14b-720p-qkv"]
+    say(f"[gpu] generating {lw.name} M={lw.M} N={lw.N} K={lw.K}")
+    x, w = synth.linear_inputs(lw)
+    xq, sx, wq, sw, y = gpu_linear(x, w)
+    MB, NB = -(-lw.M // 128), -(-lw.N // 128)
+    rblocks = [0, MB // 2, MB - 1]  # the last one is ragged (75600 = 590*128 + 80)
+    cblocks = [0, NB // 2, NB - 1]
+    sx_h, sw_h = sx.cpu().numpy(), sw.cpu().numpy()
+    for rb in rblocks:
+        rows = slice(rb * 128, min(lw.M, (rb + 1) * 128))
+        rxq, rsx = oracle.quant_b128(x[rows])
+        assert np.array_equal(xq[rows].cpu().numpy(), rxq)
+        assert np.array_equal(sx_h[rb:rb + 1].view(np.uint32), rsx.view(np.uint32))
+        for cb in cblocks:
+            cols = slice(cb * 128, min(lw.N, (cb + 1) * 128))
+            rwq, rsw = oracle.quant_b128(w[cols])
+            if rb == rblocks[0]:
+                assert np.array_equal(wq[cols].cpu().numpy(), rwq)
+                assert np.array_equal(sw_h[cb:cb + 1].view(np.uint32), rsw.view(np.uint32))
+            _, ry = oracle.w8a8_gemm(rxq, rsx, rwq, rsw)
+            got = host_u16(y[rows, cols])
+            assert np.array_equal(got, ry), (rb, cb, int((got != ry).sum()))
+    say(f"[parity] w8a8 {lw.name}: {len(rblocks) * len(cblocks)} sampled 128x128 output blocks bit-exact")
