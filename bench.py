@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b-720p]
                     [--qk int8|bf16]
+    python bench.py --op w8a8 [--linear wan14b-720p-qkv]   (the W8A8 linear layer)
 
 One step = the whole forward (sla_quantize, then sla_prepare_kv and
 sla_attend) over one batch of seeded synthetic inputs already resident in
@@ -109,6 +110,84 @@ def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True):
     }
 
 
+def bench_w8a8(args, dev):
+    """One step = quantise the activations (block-128 INT8) + the block-scaled
+    INT8 GEMM, weights quantised once beforehand (as a deployed layer keeps
+    them).  Roofline: dense INT8 MFMA peak for the GEMM's 2*M*N*K ops."""
+    import torch
+    from sparse_bit_attention_amd import sla
+    lw = synth.LINEAR_WORKLOADS[args.linear]
+    log(f"[bench] generating {lw.name} inputs")
+    x, w = synth.linear_inputs(lw)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = up(x), up(w)
+    wq, sw = sla.quant_b128(W)
+    xq = torch.empty((lw.M, lw.K), dtype=torch.int8, device=dev)
+    sx = torch.empty(((lw.M + 127) // 128, lw.K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((lw.M, lw.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    import ctypes
+    L = sla.lib()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sla._check(L.sla_quant_b128(ctypes.c_void_p(X.data_ptr()), lw.M, lw.K,
+                                    ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream)), "sla_quant_b128")
+        if ev is not None:
+            ev[1].record(stream)
+        sla.w8a8_gemm(xq, sx, wq, sw, out=y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ops = 2.0 * lw.M * lw.N * lw.K
+    log(f"[bench] ms/step {ms_step:.3f} (quantize X {q_ms:.3f}, gemm {g_ms:.3f})")
+    res = {
+        "metric": "W8A8 block-128 linear layer TOPS (INT8 MFMA), Wan-14B-720P projection shape",
+        "value": ops / (ms_step * 1e-3) / 1e12,
+        "unit": "TOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": lw.name, "M": lw.M, "N": lw.N, "K": lw.K, "block": 128},
+        "stage_ms": {"sla_quant_b128(X)": q_ms, "sla_w8a8_gemm": g_ms},
+        "roofline": {"kernel": "k_w8a8_gemm", "bound": "mfma", "achieved": ops / (g_ms * 1e-3) / 1e12,
+                     "peak": P_I8 / 1e12, "unit": "TOP/s",
+                     "frac": ops / (g_ms * 1e-3) / P_I8, "traffic": None},
+    }
+    if args.cpu_blocks > 0:
+        # the oracle on a sample: rows of one 128-row block against all N columns
+        import oracle
+        t1 = time.perf_counter()
+        rxq, rsx = oracle.quant_b128(x[:128])
+        rwq, rsw = oracle.quant_b128(w)
+        t2 = time.perf_counter()
+        nrow = min(args.cpu_blocks // 60 + 1, 4)
+        oracle.w8a8_gemm(rxq[:nrow], rsx, rwq, rsw)
+        t3 = time.perf_counter()
+        sample_ops = 2.0 * nrow * lw.N * lw.K
+        res["cpu_baseline"] = {
+            "value": sample_ops / (t3 - t2) / 1e12, "unit": "TOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nrow} rows x all {lw.N} columns of the GEMM ({t3 - t2:.1f}s; quantisation "
+                      f"of 128 X rows and all of W {t2 - t1:.1f}s not counted), single thread"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +198,9 @@ def main():
                     help="query blocks the CPU oracle baseline computes (0 = skip)")
     ap.add_argument("--qk", choices=("int8", "bf16"), default="int8",
                     help="QK^T operands: int8 (SageSLA, the default) or bf16 (plain SLA)")
+    ap.add_argument("--op", choices=("sagesla", "w8a8"), default="sagesla",
+                    help="sagesla: the attention forward (default); w8a8: the W8A8 linear layer")
+    ap.add_argument("--linear", default="wan14b-720p-qkv", choices=sorted(synth.LINEAR_WORKLOADS))
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -144,6 +226,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.op == "w8a8":
+        bench_w8a8(args, dev)
         return
 
     wl = synth.WORKLOADS[args.workload]

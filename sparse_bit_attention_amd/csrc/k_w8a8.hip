@@ -13,8 +13,8 @@
 //   per SIMD) of 64 x 64; per K block of 128 the exact int32 products come
 //   from v_mfma_i32_16x16x64_i8 and are folded into float32 accumulators with
 //   one fma by the block's scale product sx * sw (float32), blocks in
-//   ascending order.  X and W tiles pass through LDS (double-buffered, rows
-//   padded to 144 bytes so the fragment reads spread over all banks).
+//   ascending order.  X and W tiles pass through LDS (double-buffered, 16-byte
+//   pieces XOR-swizzled by row so the fragment reads spread over all banks).
 //
 // On gfx950 the fold costs two vector ALU instructions per output element per
 // K block (convert, fma): as much issue time as the block's MFMAs, so the
@@ -83,8 +83,16 @@ __global__ __launch_bounds__(256) void k_quant_b128(const uint16_t *__restrict__
 }
 
 constexpr int GM_BM = 128, GM_BN = 256, GM_BK = 128;
-constexpr int GM_G = 16;              // row tiles per ordering group
-constexpr int GM_PITCH = GM_BK + 16;  // bytes per LDS row
+constexpr int GM_G = 4;               // row tiles per ordering group
+constexpr int GM_PITCH = GM_BK;       // bytes per LDS row
+// LDS byte offset of the 16 bytes lane l reads for an MFMA operand: row
+// row0 + l%16, k chunk kc, bytes 64 kc + 16 (l/16) of the row; the 16-byte
+// pieces of a row are XOR-swizzled by its index, so the 16 rows of a
+// fragment, and the 8 pieces of a row, fall on distinct banks.
+__device__ __forceinline__ int lds_off(int row0, int kc, int lane) {
+  const int row = row0 + (lane & 15);
+  return row * GM_PITCH + 16 * ((4 * kc + (lane >> 4)) ^ (row & 7));
+}
 
 __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__ xq,
                                                       const float *__restrict__ sx,
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
 #pragma unroll
     for (int it = 0; it < 6; ++it) {
       const int q = it * 512 + tid, row = q >> 3, pc = q & 7;
-      *(uint4 *)(&lds[s][row * GM_PITCH + 16 * pc]) = stg[it];
+      *(uint4 *)(&lds[s][row * GM_PITCH + 16 * (pc ^ (row & 7))]) = stg[it];
     }
   };
 
@@ -145,31 +153,36 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
     if (kb + 1 < KB) gload(kb + 1);
     // exact int32 block products: lane (row 16 i + l%16, group g) reads
     // bytes 64 kc + 16 g .. +15 of its row
-    v4i ia[4][4];
+    v4i af[4][2], bf[4][2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      v4i af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const v4i *)(&lds[s][(64 * wr + 16 * i + (lane & 15)) * GM_PITCH + 64 * kc + 16 * (lane >> 4)]);
+      for (int i = 0; i < 4; ++i) af[i][kc] = *(const v4i *)(&lds[s][lds_off(64 * wr + 16 * i, kc, lane)]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j] = *(const v4i *)(&lds[s][(GM_BM + 64 * wc + 16 * j + (lane & 15)) * GM_PITCH + 64 * kc +
-                                       16 * (lane >> 4)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ia[i][j] = mfma_i8(af[i], bf[j], kc == 0 ? v4i{0, 0, 0, 0} : ia[i][j]);
+        bf[j][kc] = *(const v4i *)(&lds[s][lds_off(GM_BM + 64 * wc + 16 * j, kc, lane)]);
     }
-    // fold the block into the float32 sums: one fma by sx * sw per element
+    // Tile t = (i, j): its two MFMAs (the exact int32 block product), then
+    // the fold of tile t-1 into the float32 sums, one fma by sx * sw per
+    // element; the fences keep this order, so the fold's vector ALU work runs
+    // while the matrix core computes the next tile.
     const float sc = sx[(size_t)mb * KB + kb] * sw[(size_t)nb * KB + kb];
+    v4i ia[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t <= 16; ++t) {
+      if (t < 16) {
+        const int i = t >> 2, j = t & 3;
+        ia[t & 1] = mfma_i8(af[i][0], bf[j][0], v4i{0, 0, 0, 0});
+        ia[t & 1] = mfma_i8(af[i][1], bf[j][1], ia[t & 1]);
+      }
+      if (t > 0) {
+        const int i = (t - 1) >> 2, j = (t - 1) & 3;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf((float)ia[i][j][r], sc, acc[i][j][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = __builtin_fmaf((float)ia[(t - 1) & 1][r], sc, acc[i][j][r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (kb + 1 < KB) lstore(s ^ 1);
     __syncthreads();
   }
