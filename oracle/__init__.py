@@ -63,6 +63,10 @@ def lib():
         L.sla_ref_linear_block.argtypes = [P, P, P, P, i32, i32, i32, P]
         L.sla_ref_combine.argtypes = [P, P, P, i32, i32, i32, P]
         L.sla_ref_quant_b128.argtypes = [P, i32, i32, P, P]
+        L.sla_ref_quant_q_g.argtypes = [P, i32, i32, i32, P, P]
+        L.sla_ref_quant_k_g.argtypes = [P, P, i32, i32, i32, P, P]
+        L.sla_ref_sparse_block_g.argtypes = [i32, P, P, P, P, i32, i32, P, P, P, i32, i32,
+                                             ctypes.c_float, P, i32, i32, P]
         L.sla_ref_w8a8_gemm.argtypes = [P, P, P, P, i32, i32, i32, P, P]
         _lib = L
     return _lib
@@ -128,25 +132,32 @@ def topk(s, kb):
     return mask, kept[:, :kb]
 
 
-def quant_q(Q):
+# Scale granularity: rows per scale group of Q and of K' (64 = one per block;
+# the finer SageAttention2++-style mode uses 16 query rows and 4 keys).
+QGROUP_FINE, KGROUP_FINE = 16, 4
+
+
+def quant_q(Q, g=BLOCK):
+    """INT8 codes [T*64, d] and scales: [T] for g = 64, else [T, 64/g]."""
     Q = _u16(Q)
     N, d = Q.shape
     T = nblocks(N)
     q8 = np.empty((T * BLOCK, d), np.int8)
-    dq = np.empty(T, np.float32)
-    lib().sla_ref_quant_q(_p(Q), N, d, _p(q8), _p(dq))
-    return q8, dq
+    dq = np.empty((T, BLOCK // g), np.float32)
+    lib().sla_ref_quant_q_g(_p(Q), N, d, g, _p(q8), _p(dq))
+    return q8, (dq[:, 0].copy() if g == BLOCK else dq)
 
 
-def quant_k(K, mu):
+def quant_k(K, mu, g=BLOCK):
+    """INT8 codes of K - mu [T*64, d] and scales: [T] for g = 64, else [T, 64/g]."""
     K = _u16(K)
     N, d = K.shape
     T = nblocks(N)
     mu = np.ascontiguousarray(mu, np.float32)
     k8 = np.empty((T * BLOCK, d), np.int8)
-    dk = np.empty(T, np.float32)
-    lib().sla_ref_quant_k(_p(K), _p(mu), N, d, _p(k8), _p(dk))
-    return k8, dk
+    dk = np.empty((T, BLOCK // g), np.float32)
+    lib().sla_ref_quant_k_g(_p(K), _p(mu), N, d, g, _p(k8), _p(dk))
+    return k8, (dk[:, 0].copy() if g == BLOCK else dk)
 
 
 def qk_int32(q8, k8, i, j):
@@ -158,7 +169,9 @@ def qk_int32(q8, k8, i, j):
 
 
 def sparse_block(i, kept_i, Q, K, V, sm_scale, q8=None, dq=None, k8=None, dk=None):
-    """Exact branch for query block i; quantised when q8/k8 are given."""
+    """Exact branch for query block i; quantised when q8/k8 are given (the
+    scale granularity follows from the shape of dq / dk: [T] per block,
+    [T, 64/g] per group of g rows)."""
     Q, K, V = _u16(Q), _u16(K), _u16(V)
     N, d = Q.shape
     kept_i = np.ascontiguousarray(kept_i, np.int32)
@@ -172,11 +185,13 @@ def sparse_block(i, kept_i, Q, K, V, sm_scale, q8=None, dq=None, k8=None, dk=Non
     ni = min(BLOCK, N - i * BLOCK)
     out = np.empty((ni, d), np.float64)
     kp = kept_i if kb else np.zeros(1, np.int32)
-    lib().sla_ref_sparse_block(int(quantized), _p(np.ascontiguousarray(q8)),
-                               _p(np.ascontiguousarray(dq, np.float32)),
-                               _p(np.ascontiguousarray(k8)),
-                               _p(np.ascontiguousarray(dk, np.float32)), _p(Q), _p(K), _p(V),
-                               N, d, ctypes.c_float(sm_scale), _p(kp), kb, i, _p(out))
+    dq = np.ascontiguousarray(dq, np.float32)
+    dk = np.ascontiguousarray(dk, np.float32)
+    gq = BLOCK // dq.shape[1] if dq.ndim == 2 else BLOCK
+    gk = BLOCK // dk.shape[1] if dk.ndim == 2 else BLOCK
+    lib().sla_ref_sparse_block_g(int(quantized), _p(np.ascontiguousarray(q8)), _p(dq),
+                                 _p(np.ascontiguousarray(k8)), _p(dk), gq, gk, _p(Q), _p(K), _p(V),
+                                 N, d, ctypes.c_float(sm_scale), _p(kp), kb, i, _p(out))
     return out
 
 
@@ -229,8 +244,9 @@ class HeadPrep:
     dk: np.ndarray
 
 
-def head_prep(Q, K, topk_frac, smooth=True) -> HeadPrep:
-    """Steps 1-6 for one head (pool, K mean, scores, top-k, Q and K INT8)."""
+def head_prep(Q, K, topk_frac, smooth=True, fine=False) -> HeadPrep:
+    """Steps 1-6 for one head (pool, K mean, scores, top-k, Q and K INT8);
+    ``fine``: SageAttention2++-style scale groups (16 query rows, 4 keys)."""
     N, d = np.shape(Q)
     T = nblocks(N)
     kb = kb_for(T, topk_frac)
@@ -241,14 +257,14 @@ def head_prep(Q, K, topk_frac, smooth=True) -> HeadPrep:
     mu = kmean(ksum, N)
     s = scores(qbar, kbar, mu)
     mask, kept = topk(s, kb)
-    q8, dq = quant_q(Q)
-    k8, dk = quant_k(K, mu if smooth else np.zeros_like(mu))
+    q8, dq = quant_q(Q, QGROUP_FINE if fine else BLOCK)
+    k8, dk = quant_k(K, mu if smooth else np.zeros_like(mu), KGROUP_FINE if fine else BLOCK)
     return HeadPrep(qsum, qbar, ksum, kbar, mu, s, mask, kept, q8, dq, k8, dk)
 
 
 def head_forward(Q, K, V, W, topk_frac, use_linear=True, sm_scale=None, blocks=None,
                  prep: HeadPrep | None = None, states=None, smooth=True, parts=False,
-                 qk_int8=True):
+                 qk_int8=True, fine=False):
     """SageSLA forward of one head in float64 for the query blocks ``blocks``
     (all by default).  Returns {i: out[n_i, d]} (and the two branches when
     ``parts``).  ``qk_int8=False`` is plain SLA: the same selection and linear
@@ -259,7 +275,7 @@ def head_forward(Q, K, V, W, topk_frac, use_linear=True, sm_scale=None, blocks=N
     if sm_scale is None:
         sm_scale = default_sm_scale(d)
     if prep is None:
-        prep = head_prep(Q, K, topk_frac, smooth=smooth)
+        prep = head_prep(Q, K, topk_frac, smooth=smooth, fine=fine)
     if use_linear and states is None:
         states = linear_states(K, V)
     res = {}

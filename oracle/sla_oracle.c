@@ -167,8 +167,27 @@ static void quant_block(const float *x /* [n][d] */, int n, int d, int8_t *codes
     }
 }
 
-/* Step 5: Q -> INT8 with one scale per 64-row block.  q8 is [T*64][d]. */
-void sla_ref_quant_q(const uint16_t *Q, int N, int d, int8_t *q8, float *dq) {
+/* One 64-row block quantised in groups of g consecutive rows (g divides 64),
+ * each group with its own scale (quant_block on the group); rows past n are
+ * padding (zero codes; a group of padding only has scale 0).  codes is
+ * [64][d], delta [64/g]. */
+static void quant_groups(const float *x /* [n][d] */, int n, int d, int g, int8_t *codes,
+                         float *delta) {
+  int8_t *tmp = (int8_t *)malloc((size_t)SLA_REF_BLOCK * d);
+  for (int q = 0; q < SLA_REF_BLOCK / g; ++q) {
+    int r0 = q * g;
+    int ng = n - r0 < 0 ? 0 : (n - r0 < g ? n - r0 : g);
+    quant_block(x + (size_t)r0 * d, ng, d, tmp, delta + q);
+    memcpy(codes + (size_t)r0 * d, tmp, (size_t)g * d);
+  }
+  free(tmp);
+}
+
+/* Step 5: Q -> INT8, one scale per group of g rows of each 64-row block (g =
+ * 64: one scale per block; g = 16: SageAttention2++-style finer scales, one
+ * per 16 queries, the rows of one matrix-core output tile).  q8 is [T*64][d],
+ * dq [T][64/g]. */
+void sla_ref_quant_q_g(const uint16_t *Q, int N, int d, int g, int8_t *q8, float *dq) {
   int T = nblocks(N);
   float *x = (float *)malloc(sizeof(float) * SLA_REF_BLOCK * d);
   for (int t = 0; t < T; ++t) {
@@ -176,14 +195,21 @@ void sla_ref_quant_q(const uint16_t *Q, int N, int d, int8_t *q8, float *dq) {
     for (int r = 0; r < n; ++r)
       for (int c = 0; c < d; ++c)
         x[(size_t)r * d + c] = bf16f(Q[(size_t)(t * SLA_REF_BLOCK + r) * d + c]);
-    quant_block(x, n, d, q8 + (size_t)t * SLA_REF_BLOCK * d, dq + t);
+    quant_groups(x, n, d, g, q8 + (size_t)t * SLA_REF_BLOCK * d, dq + (size_t)t * (SLA_REF_BLOCK / g));
   }
   free(x);
 }
 
+void sla_ref_quant_q(const uint16_t *Q, int N, int d, int8_t *q8, float *dq) {
+  sla_ref_quant_q_g(Q, N, d, SLA_REF_BLOCK, q8, dq);
+}
+
 /* Step 6: K smoothing then INT8.  k' = float32(K - mu[c]) (mu = 0 turns the
- * smoothing off), then one scale per 64-row block as for Q. */
-void sla_ref_quant_k(const uint16_t *K, const float *mu, int N, int d, int8_t *k8, float *dk) {
+ * smoothing off), then one scale per group of g rows as for Q (g = 64: per
+ * block; g = 4: the finer, "thread-level" scales of SageAttention2++, one per
+ * 4 keys).  dk is [T][64/g]. */
+void sla_ref_quant_k_g(const uint16_t *K, const float *mu, int N, int d, int g, int8_t *k8,
+                       float *dk) {
   int T = nblocks(N);
   float *x = (float *)malloc(sizeof(float) * SLA_REF_BLOCK * d);
   for (int t = 0; t < T; ++t) {
@@ -191,9 +217,13 @@ void sla_ref_quant_k(const uint16_t *K, const float *mu, int N, int d, int8_t *k
     for (int r = 0; r < n; ++r)
       for (int c = 0; c < d; ++c)
         x[(size_t)r * d + c] = bf16f(K[(size_t)(t * SLA_REF_BLOCK + r) * d + c]) - mu[c];
-    quant_block(x, n, d, k8 + (size_t)t * SLA_REF_BLOCK * d, dk + t);
+    quant_groups(x, n, d, g, k8 + (size_t)t * SLA_REF_BLOCK * d, dk + (size_t)t * (SLA_REF_BLOCK / g));
   }
   free(x);
+}
+
+void sla_ref_quant_k(const uint16_t *K, const float *mu, int N, int d, int8_t *k8, float *dk) {
+  sla_ref_quant_k_g(K, mu, N, d, SLA_REF_BLOCK, k8, dk);
 }
 
 /* Step 7: int32 scores of query block i against key block j,
@@ -211,14 +241,15 @@ void sla_ref_qk_int32(const int8_t *q8, const int8_t *k8, int d, int i, int j, i
 
 /* Step 8, the exact (softmax) branch for the valid rows of query block i,
  * restricted to its kept key blocks.  Quantised mode (quantized != 0): logit
- * = A * dq_i * dk_j * sm_scale from the INT8 codes.  Exact mode: logit =
- * (Q_r . K_s) * sm_scale from the bf16 inputs in float64.  Padding keys are
- * excluded.  Softmax in float64 with the row maximum subtracted; out is
- * [n_i][d]; all zeros when kb = 0. */
-void sla_ref_sparse_block(int quantized, const int8_t *q8, const float *dq, const int8_t *k8,
-                          const float *dk, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
-                          int N, int d, float sm_scale, const int32_t *kept_i, int kb, int i,
-                          double *out) {
+ * = A[r][s] * dq(i, r) * dk(j, s) * sm_scale from the INT8 codes, the scales
+ * of the row groups (gq query rows, gk keys; 64 = one per block) holding r
+ * and s.  Exact mode: logit = (Q_r . K_s) * sm_scale from the bf16 inputs in
+ * float64.  Padding keys are excluded.  Softmax in float64 with the row
+ * maximum subtracted; out is [n_i][d]; all zeros when kb = 0. */
+void sla_ref_sparse_block_g(int quantized, const int8_t *q8, const float *dq, const int8_t *k8,
+                            const float *dk, int gq, int gk, const uint16_t *Q, const uint16_t *K,
+                            const uint16_t *V, int N, int d, float sm_scale, const int32_t *kept_i,
+                            int kb, int i, double *out) {
   int ni = rows_in(i, N);
   size_t nl = (size_t)kb * SLA_REF_BLOCK; /* logits per row */
   double *lg = (double *)malloc(sizeof(double) * (size_t)SLA_REF_BLOCK * (nl ? nl : 1));
@@ -234,7 +265,8 @@ void sla_ref_sparse_block(int quantized, const int8_t *q8, const float *dq, cons
         double l = -INFINITY;
         if (s < nj) {
           if (quantized) {
-            l = (double)A[r * SLA_REF_BLOCK + s] * (double)dq[i] * (double)dk[j] * (double)sm_scale;
+            l = (double)A[r * SLA_REF_BLOCK + s] * (double)dq[i * (SLA_REF_BLOCK / gq) + r / gq] *
+                (double)dk[j * (SLA_REF_BLOCK / gk) + s / gk] * (double)sm_scale;
           } else {
             double dot = 0.0;
             for (int c = 0; c < d; ++c)
@@ -268,6 +300,14 @@ void sla_ref_sparse_block(int quantized, const int8_t *q8, const float *dq, cons
   free(lg);
   free(A);
   free(acc);
+}
+
+void sla_ref_sparse_block(int quantized, const int8_t *q8, const float *dq, const int8_t *k8,
+                          const float *dk, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                          int N, int d, float sm_scale, const int32_t *kept_i, int kb, int i,
+                          double *out) {
+  sla_ref_sparse_block_g(quantized, q8, dq, k8, dk, SLA_REF_BLOCK, SLA_REF_BLOCK, Q, K, V, N, d,
+                         sm_scale, kept_i, kb, i, out);
 }
 
 /* The linear-attention feature map phi.  The pages only say "kernel-function
