@@ -1,7 +1,7 @@
 """SageSLA forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b-720p]
-                    [--qk int8|bf16]
+                    [--qk int8|int8-fine|bf16]
     python bench.py --op w8a8 [--linear wan14b-720p-qkv]   (the W8A8 linear layer)
 
 One step = the whole forward (sla_quantize, then sla_prepare_kv and
@@ -75,7 +75,7 @@ def traffic_entry():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True):
+def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True, fine=False):
     """The oracle, single threaded, on one head of the workload: the head's
     whole selection/quantisation and linear states plus n_blocks query blocks;
     the head time is extrapolated to all T query blocks and reported as
@@ -85,7 +85,7 @@ def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True):
     w = synth.proj_weight(wl)
     T = oracle.nblocks(wl.N)
     t0 = time.perf_counter()
-    prep = oracle.head_prep(q, k, float(np.float32(wl.topk)))
+    prep = oracle.head_prep(q, k, float(np.float32(wl.topk)), fine=fine)
     states = oracle.linear_states(k, v) if wl.use_linear else None
     t1 = time.perf_counter()
     rng = np.random.default_rng(0)
@@ -196,8 +196,10 @@ def main():
     ap.add_argument("--workload", default="wan14b-720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-blocks", type=int, default=360,
                     help="query blocks the CPU oracle baseline computes (0 = skip)")
-    ap.add_argument("--qk", choices=("int8", "bf16"), default="int8",
-                    help="QK^T operands: int8 (SageSLA, the default) or bf16 (plain SLA)")
+    ap.add_argument("--qk", choices=("int8", "int8-fine", "bf16"), default="int8",
+                    help="QK^T operands: int8 (SageSLA with one scale per 64-row block, the "
+                         "default), int8-fine (one Q scale per 16 rows, one K scale per 4 "
+                         "keys) or bf16 (plain SLA)")
     ap.add_argument("--op", choices=("sagesla", "w8a8"), default="sagesla",
                     help="sagesla: the attention forward (default); w8a8: the W8A8 linear layer")
     ap.add_argument("--linear", default="wan14b-720p-qkv", choices=sorted(synth.LINEAR_WORKLOADS))
@@ -243,9 +245,10 @@ def main():
     Q, K, V, W = up(q), up(k), up(v), up(w)
     del q, k, v
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
-    qk_int8 = args.qk == "int8"
+    qk_int8 = args.qk != "bf16"
+    fine = args.qk == "int8-fine"
     m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear), device=dev,
-                    qk_int8=qk_int8)
+                    qk_int8=qk_int8, qk_fine=fine)
     T, kb = m.plan.info.T, m.plan.info.kb
     out = torch.empty_like(Q)
     Wp = W if wl.use_linear else None
@@ -288,7 +291,7 @@ def main():
     t_roof_attn = i8 / P_I8 + bf / P_BF16
     blended_peak = (i8 + bf) / t_roof_attn
     achieved = (i8 + bf) / (at_ms * 1e-3)
-    traffic = traffic_entry() if qk_int8 else None
+    traffic = traffic_entry() if args.qk == "int8" else None
 
     res = {
         "metric": METRIC,
@@ -321,7 +324,7 @@ def main():
     }
     if args.cpu_blocks > 0:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks, qk_int8=qk_int8)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks, qk_int8=qk_int8, fine=fine)
     print(json.dumps(res), flush=True)
 
 

@@ -73,6 +73,9 @@ typedef struct {
   int32_t use_linear;  /* 1: add the projected linear branch; 0: sparse branch only */
   float sm_scale;      /* softmax scale; 0 selects float32(1/sqrt(d)) */
   int32_t qk_int8;     /* 1: INT8 QK^T (SageSLA); 0: bf16 QK^T (plain SLA); else EINVAL */
+  int32_t qk_fine;     /* INT8 scale granularity: 0 one scale per 64-row block; 1 the
+                          SageAttention2++-style thread-level scales, one per 16 query
+                          rows and one per 4 keys (needs qk_int8 = 1); else EINVAL */
 } sla_config;
 
 typedef struct sla_plan_s *sla_plan_t;
@@ -132,8 +135,10 @@ enum {
                       holds row r, channel c                                      */
   SLA_WS_K8 = 7,   /* int8, same layout as Q8, of K - mu (Q8, K8: 0 bytes when
                       qk_int8 = 0)                                                */
-  SLA_WS_DQ = 8,   /* float [B*H][T] Q block scales                               */
-  SLA_WS_DK = 9,   /* float [B*H][T] K' block scales (1 when qk_int8 = 0)         */
+  SLA_WS_DQ = 8,   /* float [B*H][T] Q block scales ([B*H][T][4] with qk_fine:
+                      one per 16 rows)                                            */
+  SLA_WS_DK = 9,   /* float [B*H][T] K' block scales (1 when qk_int8 = 0;
+                      [B*H][T][16] with qk_fine: one per 4 keys)                  */
   SLA_WS_COUNT = 10
 };
 

@@ -100,10 +100,11 @@ constexpr float SCORE_BIAS = 12582912.0f;
 constexpr float BIAS_C_LIMIT = 0x1p-10f;
 
 // Probabilities of one 32-key half for query tile U as a bf16 B fragment (k
-// order of kmaj_off) and their sum: p = exp2(score * c - m).
+// order of kmaj_off) and their sum: p = exp2(score * c - m), c = c0 for the
+// half's first key tile, c1 for its second.
 template <int U, bool BIASED>
-__device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m, float &lsum) {
-  const float nm = BIASED ? -__builtin_fmaf(SCORE_BIAS, c, m) : -m;
+__device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c0, float c1, float m,
+                                          float &lsum) {
   const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
   // The pairs stay in scalars: bit-casting an element of an ext-vector is
   // miscompiled by this clang (every element reads element 0).
@@ -114,6 +115,8 @@ __device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m
     const int a0 = s[e0 >> 2][U][e0 & 3], a1 = s[e1 >> 2][U][e1 & 3];
     const float f0 = BIASED ? __int_as_float(a0) : (float)a0;
     const float f1 = BIASED ? __int_as_float(a1) : (float)a1;
+    const float c = h < 2 ? c0 : c1;  // elements 0..3: first tile, 4..7: second
+    const float nm = BIASED ? -__builtin_fmaf(SCORE_BIAS, c, m) : -m;
     const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(f0, c, nm));
     const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(f1, c, nm));
     pk[h] = pack2bf(x0, x1);
@@ -125,12 +128,13 @@ __device__ __forceinline__ v4u probs_half(const v4i (&s)[2][4], float c, float m
 // One kept key block, in two 32-key halves (QK^T half -> probabilities -> PV
 // half).  BOUND: m is an upper bound of every logit of the row (set before the
 // loop): no running max, no rescaling.  Otherwise m is a running max, moved
-// lazily per half.
+// lazily per half.  The logit scale of query tile u and key tile t (this
+// lane's keys of it) is cq[u] * ck[t].
 template <int D, bool BOUND>
 __device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf)[4][D / 64],
                                              v4f (&o)[D / 16][4], float (&m)[4],
-                                             float (&lsum)[4], float c, bool last,
-                                             int npad_lane) {
+                                             float (&lsum)[4], const float (&cq)[4],
+                                             const float (&ck)[4], bool last, int npad_lane) {
   constexpr int KC = D / 64, CG = D / 16;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -147,21 +151,23 @@ __device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf
         s[t2][u] = acc;
       }
     if (!BOUND) {
-      // half-tile max per query (padding keys score 0 and may only raise it)
-      int imax[4];
+      // half-tile max logit per query (padding keys score 0 and may only raise
+      // it); the scales are positive, so each tile's max logit is at its max
+      // score
+      float lmax[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int a0 = max(max(s[0][u][0], s[0][u][1]), s[0][u][2]);
-        const int a1 = max(max(s[0][u][3], s[1][u][0]), s[1][u][1]);
-        imax[u] = max(max(a0, a1), max(s[1][u][2], s[1][u][3]));
+        const int a0 = max(max(s[0][u][0], s[0][u][1]), max(s[0][u][2], s[0][u][3]));
+        const int a1 = max(max(s[1][u][0], s[1][u][1]), max(s[1][u][2], s[1][u][3]));
+        lmax[u] = fmaxf((float)a0 * (cq[u] * ck[2 * hf]), (float)a1 * (cq[u] * ck[2 * hf + 1]));
       }
       bool need = false;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) need |= ((float)imax[u] * c > m[u] + RESCALE_SLACK);
+      for (int u = 0; u < 4; ++u) need |= (lmax[u] > m[u] + RESCALE_SLACK);
       if (__ballot(need) != 0ull) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          float tm = (float)imax[u] * c;
+          float tm = lmax[u];
           tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
           tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
           if (tm > m[u] + RESCALE_SLACK) {
@@ -175,10 +181,10 @@ __device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf
       }
     }
     v4u pf[4];
-    pf[0] = probs_half<0, BOUND>(s, c, m[0], lsum[0]);
-    pf[1] = probs_half<1, BOUND>(s, c, m[1], lsum[1]);
-    pf[2] = probs_half<2, BOUND>(s, c, m[2], lsum[2]);
-    pf[3] = probs_half<3, BOUND>(s, c, m[3], lsum[3]);
+    pf[0] = probs_half<0, BOUND>(s, cq[0] * ck[2 * hf], cq[0] * ck[2 * hf + 1], m[0], lsum[0]);
+    pf[1] = probs_half<1, BOUND>(s, cq[1] * ck[2 * hf], cq[1] * ck[2 * hf + 1], m[1], lsum[1]);
+    pf[2] = probs_half<2, BOUND>(s, cq[2] * ck[2 * hf], cq[2] * ck[2 * hf + 1], m[2], lsum[2]);
+    pf[3] = probs_half<3, BOUND>(s, cq[3] * ck[2 * hf], cq[3] * ck[2 * hf + 1], m[3], lsum[3]);
 #pragma unroll
     for (int a = 0; a < CG; ++a)
 #pragma unroll
@@ -189,6 +195,7 @@ __device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       // the same arithmetic the probabilities of a zero score went through
+      const float c = cq[u] * ck[3];  // the last tile holds every padding key
       const float xz = BOUND ? __builtin_fmaf(SCORE_BIAS, c, -__builtin_fmaf(SCORE_BIAS, c, m[u]))
                              : -m[u];
       const uint32_t pp = pack2bf(__builtin_amdgcn_exp2f(xz), 0.f);
@@ -200,13 +207,21 @@ __device__ __forceinline__ void attend_block(const KVBlock<D> &x, const v4i (&qf
 // The kept-block loop.  Two register sets alternate: the loads of block n+1
 // are issued before block n is computed, so each load has a whole block of
 // work to land, and no operand passes through LDS.
-template <int D, bool BOUND>
+// dqi[u]: dq of query tile u times sm_scale log2(e); FINE: dk holds 16 scales
+// per key block (one per 4 keys), this lane's keys of tile t use scale 4t + g.
+template <int D, bool BOUND, bool FINE>
 __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D / 16][4],
                                           float (&m)[4], float (&lsum)[4], const int32_t *kl,
                                           int kb, const float *dk, const uint4 *k8u,
-                                          const uint4 *vtu, size_t headblk, float dqi, int T,
-                                          int npad_lane, int lane) {
+                                          const uint4 *vtu, size_t headblk, const float (&dqi)[4],
+                                          int T, int npad_lane, int lane) {
   if (kb <= 0) return;
+  auto kscales = [&](int j, float (&ck)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      ck[t] = FINE ? dk[(headblk + j) * 16 + 4 * t + (lane >> 4)] : dk[headblk + j];
+  };
+  float cka[4], ckb[4];
   KVBlock<D> xa, xb;
   load_kv<D>(xa, k8u, vtu, headblk + kl[0], lane);
   int n = 0;
@@ -217,15 +232,18 @@ __device__ __forceinline__ void kept_loop(const v4i (&qf)[4][D / 64], v4f (&o)[D
     __builtin_amdgcn_sched_barrier(0);
     load_kv<D>(xb, k8u, vtu, headblk + jb, lane);
     __builtin_amdgcn_sched_barrier(0);
-    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi * dk[headblk + ja], ja == T - 1, npad_lane);
+    kscales(ja, cka);
+    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi, cka, ja == T - 1, npad_lane);
     __builtin_amdgcn_sched_barrier(0);
     if (n + 2 < kb) load_kv<D>(xa, k8u, vtu, headblk + kl[n + 2], lane);
     __builtin_amdgcn_sched_barrier(0);
-    attend_block<D, BOUND>(xb, qf, o, m, lsum, dqi * dk[headblk + jb], jb == T - 1, npad_lane);
+    kscales(jb, ckb);
+    attend_block<D, BOUND>(xb, qf, o, m, lsum, dqi, ckb, jb == T - 1, npad_lane);
   }
   if (n < kb) {
     const int ja = kl[n];
-    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi * dk[headblk + ja], ja == T - 1, npad_lane);
+    kscales(ja, cka);
+    attend_block<D, BOUND>(xa, qf, o, m, lsum, dqi, cka, ja == T - 1, npad_lane);
   }
 }
 
@@ -308,12 +326,16 @@ struct PipeBlocks {
   float c[2];         // logit scale of block 2i, 2i+1
   float nm[2][4];     // QKOps::nm(c, m_u); -inf for a block past the kept list
   int last[3];        // block 2i-1, 2i, 2i+1 is the head's last (ragged) block
+  // finer INT8 scales: this lane's key scale of each tile of block 2i, 2i+1,
+  // the query-tile factors, the row bounds, and which blocks are real
+  float ck[2][4], dq[4], m[4];
+  int valid[2];
 };
 
 // Sub-stage R (0..7) of the loop body; sigma = 8 i + R.
 // lm[h]: the ones fragment for half h of the head's last block, zero at its
 // padding keys, so the row sums leave those keys out.
-template <int D, bool QK8, int R>
+template <int D, bool QK8, bool FINE, int R>
 __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
                                           const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK],
                                           const PipeBlocks &pb, const v4u (&lm)[2],
@@ -356,7 +378,19 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
   constexpr int chf = ((R / 2) + 1) & 1;
   const v4u ones = {BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR, BF16_ONE_PAIR};
   const v4u rs = pb.last[cblk] ? lm[chf] : ones;
-  const float c = pb.c[blk];
+  // logit scale and exp2 offset per query tile: one per block, or (FINE) the
+  // query tile's factor times this lane's key-group scale of tile R % 4
+  float cu[4], nmu[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if constexpr (FINE) {
+      cu[u] = pb.dq[u] * pb.ck[blk][R & 3];
+      nmu[u] = pb.valid[blk] ? Q::nm(cu[u], pb.m[u]) : -INFINITY;
+    } else {
+      cu[u] = pb.c[blk];
+      nmu[u] = pb.nm[blk][u];
+    }
+  }
   constexpr int NSLOT = NM > 16 ? NM : 16;  // d = 64 has fewer MFMAs than scores on odd R
   uint32_t xs[4][4];
 #pragma unroll
@@ -378,7 +412,7 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
       // the float32 (one byte permute per pair)
       const int u = i / 4, r = i % 4;
       xs[u][r] = __float_as_uint(
-          __builtin_amdgcn_exp2f(__builtin_fmaf(Q::score(st.s[R & 1][u], r), c, pb.nm[blk][u])));
+          __builtin_amdgcn_exp2f(__builtin_fmaf(Q::score(st.s[R & 1][u], r), cu[u], nmu[u])));
       if (r == 3) {
         // bytes 2,3 of the first value, then bytes 2,3 of the second
         const uint32_t p0 = __builtin_amdgcn_perm(xs[u][1], xs[u][0], 0x07060302u);
@@ -397,11 +431,14 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
 }
 
 // K fragments come from k8u (QK8: INT8 codes) or the bf16 copy (bfk_off).
-template <int D, bool QK8>
+// dqi[u]: the query tile's scale factor (all equal unless FINE); FINE: dk
+// holds 16 scales per key block, this lane's keys of tile t use 4t + g.
+template <int D, bool QK8, bool FINE>
 __device__ __forceinline__ void kept_loop_piped(
     const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK], v4f (&o)[D / 16][4],
     const float (&m)[4], float (&lsum)[4], const int32_t *kl, int kb, const float *dk,
-    const uint4 *k8u, const uint4 *vtu, size_t headblk, float dqi, int T, int nlast, int lane) {
+    const uint4 *k8u, const uint4 *vtu, size_t headblk, const float (&dqi)[4], int T, int nlast,
+    int lane) {
   using P = Pipe<D, QK8>;
   using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, CG = P::CG, VQ = P::VQ, KT = P::KT;
@@ -480,13 +517,47 @@ __device__ __forceinline__ void kept_loop_piped(
   auto kle = [&](int n) { return kl[n < kb ? n : kb - 1]; };
   int jb[4] = {kle(0), kle(1), kle(2), kle(3)};
   int jprev = -1;  // kept entry of block 2 it - 1
-  float cb[2] = {dqi * dk[headblk + jb[0]], dqi * dk[headblk + jb[1]]};
+  const int g = lane >> 4;
+  // FINE: this lane's key scale of each tile of a block (one per 4 keys)
+  auto kscales = [&](int j, float (&ck)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ck[t] = dk[(headblk + j) * 16 + 4 * t + g];
+  };
+  float cb[2] = {0.f, 0.f};
+  float ckc[2][4];
+  if constexpr (FINE) {
+    kscales(jb[0], ckc[0]);
+    kscales(jb[1], ckc[1]);
+  } else {
+    cb[0] = dqi[0] * dk[headblk + jb[0]];
+    cb[1] = dqi[0] * dk[headblk + jb[1]];
+  }
   const int iters = (kb + 1) >> 1;
   for (int it = 0; it < iters; ++it) {
     // issued here, first read at the end of the iteration
     const int jn4 = kle(2 * it + 4), jn5 = kle(2 * it + 5);
-    const float dk2 = dk[headblk + jb[2]], dk3 = dk[headblk + jb[3]];
+    float dk2 = 0.f, dk3 = 0.f, ckn[2][4];
+    if constexpr (FINE) {
+      kscales(jb[2], ckn[0]);
+      kscales(jb[3], ckn[1]);
+    } else {
+      dk2 = dk[headblk + jb[2]];
+      dk3 = dk[headblk + jb[3]];
+    }
     PipeBlocks pb;
+    if constexpr (FINE) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pb.dq[u] = dqi[u];
+        pb.m[u] = m[u];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pb.valid[e] = 2 * it + e < kb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pb.ck[e][t] = ckc[e][t];
+      }
+    }
     pb.last[0] = jprev == T - 1;
     pb.last[1] = jb[0] == T - 1;
     pb.last[2] = jb[1] == T - 1;
@@ -501,7 +572,7 @@ __device__ __forceinline__ void kept_loop_piped(
 #define SLA_SRC(base, FR, PER, R, LEAD) \
     ((base) + ((headblk + jb[((R) + (LEAD)) >> 2]) * (FR) + (((R) + (LEAD)) & 3) * (PER)) * 64)
 #define SLA_SUB(R) \
-    sub_stage<D, QK8, R>(st, qf, pb, lm, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
+    sub_stage<D, QK8, FINE, R>(st, qf, pb, lm, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
     SLA_SUB(0);
     SLA_SUB(1);
     SLA_SUB(2);
@@ -517,8 +588,16 @@ __device__ __forceinline__ void kept_loop_piped(
     jb[1] = jb[3];
     jb[2] = jn4;
     jb[3] = jn5;
-    cb[0] = dqi * dk2;
-    cb[1] = dqi * dk3;
+    if constexpr (FINE) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ckc[0][t] = ckn[0][t];
+        ckc[1][t] = ckn[1][t];
+      }
+    } else {
+      cb[0] = dqi[0] * dk2;
+      cb[1] = dqi[0] * dk3;
+    }
   }
   // drain: PV of the last chunk (parity 1, half 1 of block 2 iters - 1) with
   // V quarters in slots 6 and 7
@@ -608,11 +687,14 @@ __device__ void exact_row_max(const v4u (&qf)[4][D / 32], const int32_t *kl, int
 // handles flagged blocks only: INT8 with the online-max loop (plain int ->
 // float scores), bf16 with the bound loop run on the rows' exact maxima.
 // QK8 = false: QK^T in bf16 from Q itself and the bf16 copy of K in kfr (no
-// INT8 step, no scales; the logit scale is sm_scale alone).
-template <int D, bool LIN, bool BOUND, bool QK8>
+// INT8 step, no scales; the logit scale is sm_scale alone).  FINE (INT8
+// only): one Q scale per 16 rows (dq [qb][4]) and one K' scale per 4 keys
+// (dk [block][16]).
+template <int D, bool LIN, bool BOUND, bool QK8, bool FINE>
 __global__ __launch_bounds__(256, 1) void k_attn(
     const int8_t *__restrict__ q8, const void *__restrict__ kfr, const float *__restrict__ dq,
-    const float *__restrict__ dk, const float *__restrict__ dkn, const uint16_t *__restrict__ vt,
+    const float *__restrict__ dk, const float *__restrict__ dkn, const float *__restrict__ dkx,
+    const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
     int32_t *__restrict__ flags, int N, int T, int kb, int nqb, int F, float qk_scale) {
@@ -630,7 +712,11 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   typename QKOps<D, QK8>::frag qf[4][KC];
   if constexpr (QK8) load_q8<D>(q8 + (size_t)qb * BLK * D, qf, lane);
   else load_qbf<D>(Q + (size_t)bh * N * D, i, N, qf, lane);
-  const float dqi = QK8 ? dq[qb] * qk_scale : qk_scale;
+  // the query tile's logit-scale factor: dq * sm_scale log2(e)
+  float dqi[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    dqi[u] = QK8 ? (FINE ? dq[(size_t)qb * 4 + u] : dq[qb]) * qk_scale : qk_scale;
 
   v4f o[CG][4];
 #pragma unroll
@@ -649,16 +735,17 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     for (int r = 0; r < 4; ++r) npad_lane += (16 * t + 4 * g + r) >= nlast;
 
   // Upper bound of the row's logits (log2 units): |q_r . k_s| <= ||q_r||
-  // ||k_s||, so logit <= dq_i sm_scale log2(e) ||q_r|| max_j (dk_j max_s ||k_s||)
-  // (INT8: codes and scales; bf16: dq = dk = 1, with a margin for the float32
-  // sums of the products and norms).
+  // ||k_s||, so logit <= dq sm_scale log2(e) ||q_r|| max_j max_s (dk_s ||k_s||)
+  // (INT8: codes and scales, dk per block or per key group; bf16: dq = dk = 1,
+  // with a margin for the float32 sums of the products and norms).
   float kmax = 0.f, dkmax = 0.f;
   for (int n = 0; n < kb; ++n) {
     const int jj = kl[n];
     kmax = fmaxf(kmax, dkn[headblk + jj]);
-    dkmax = fmaxf(dkmax, dk[headblk + jj]);
+    if (QK8) dkmax = fmaxf(dkmax, dkx[headblk + jj]);
   }
-  bool bounded = !QK8 || dqi * dkmax <= BIAS_C_LIMIT;
+  const float dqmax = fmaxf(fmaxf(dqi[0], dqi[1]), fmaxf(dqi[2], dqi[3]));
+  bool bounded = !QK8 || dqmax * dkmax <= BIAS_C_LIMIT;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float qn;
@@ -693,7 +780,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       sq += __shfl_xor(sq, 32, 64);
       qn = sqrtf(sq) * (1.0f + 0x1p-12f);
     }
-    m[u] = dqi * qn * kmax;
+    m[u] = dqi[u] * qn * kmax;
     lsum[u] = 0.f;
     bounded = bounded && (m[u] <= BOUND_LIMIT);
   }
@@ -701,17 +788,17 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const bool fail = __ballot(!bounded) != 0ull;
     if (lane == 0) flags[qb] = fail ? 1 : 0;
     if (fail) return;
-    kept_loop_piped<D, QK8>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt,
-                            headblk, dqi, T, nlast, lane);
+    kept_loop_piped<D, QK8, FINE>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr,
+                                  (const uint4 *)vt, headblk, dqi, T, nlast, lane);
   } else if constexpr (QK8) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) m[u] = -INFINITY;
-    kept_loop<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt, headblk,
-                        dqi, T, npad_lane, lane);
+    kept_loop<D, false, FINE>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt,
+                              headblk, dqi, T, npad_lane, lane);
   } else {
-    exact_row_max<D>(qf, kl, kb, (const uint4 *)kfr, headblk, T, nlast, dqi, m, lane);
-    kept_loop_piped<D, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr, (const uint4 *)vt,
-                              headblk, dqi, T, nlast, lane);
+    exact_row_max<D>(qf, kl, kb, (const uint4 *)kfr, headblk, T, nlast, dqi[0], m, lane);
+    kept_loop_piped<D, false, false>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr,
+                                     (const uint4 *)vt, headblk, dqi, T, nlast, lane);
   }
   // Row sums; O is normalised only while it is stored, so the accumulators
   // are not touched by vector ALU code in between (they stay in AGPRs).
@@ -873,42 +960,46 @@ __global__ __launch_bounds__(64) void k_debug_qk(const int8_t *__restrict__ q8,
       for (int r = 0; r < 4; ++r) o[(16 * u + l16) * BLK + 16 * t + 4 * g + r] = s[t][u][r];
 }
 
-template <int D, bool LIN, bool QK8>
+template <int D, bool LIN, bool QK8, bool FINE>
 static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
                           hipStream_t st) {
   const int nqb = p.BH * p.T;
   dim3 grid((nqb + 3) / 4), block(256);
   const float qk_scale = p.sm_scale * LOG2E;
   const void *kfr = QK8 ? (const void *)ws.k8 : (const void *)ws.kbf;
-  hipLaunchKernelGGL((k_attn<D, LIN, true, QK8>), grid, block, 0, st, ws.q8, kfr, ws.dq, ws.dk,
-                     ws.dkn, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb,
-                     p.F, qk_scale);
-  hipLaunchKernelGGL((k_attn<D, LIN, false, QK8>), grid, block, 0, st, ws.q8, kfr, ws.dq, ws.dk,
-                     ws.dkn, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N, p.T, p.kb, nqb,
-                     p.F, qk_scale);
+  hipLaunchKernelGGL((k_attn<D, LIN, true, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
+                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N,
+                     p.T, p.kb, nqb, p.F, qk_scale);
+  hipLaunchKernelGGL((k_attn<D, LIN, false, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
+                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N,
+                     p.T, p.kb, nqb, p.F, qk_scale);
 }
 
-template <int D, bool QK8>
+template <int D, bool QK8, bool FINE>
 static void launch_attn_d(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
                           hipStream_t st) {
   if (p.lin_on)
-    launch_attn_t<D, true, QK8>(p, q, ws, out, st);
+    launch_attn_t<D, true, QK8, FINE>(p, q, ws, out, st);
   else
-    launch_attn_t<D, false, QK8>(p, q, ws, out, st);
+    launch_attn_t<D, false, QK8, FINE>(p, q, ws, out, st);
+}
+
+template <int D>
+static void launch_attn_m(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
+                          hipStream_t st) {
+  if (!p.qk_int8)
+    launch_attn_d<D, false, false>(p, q, ws, out, st);
+  else if (p.qk_fine)
+    launch_attn_d<D, true, true>(p, q, ws, out, st);
+  else
+    launch_attn_d<D, true, false>(p, q, ws, out, st);
 }
 
 void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st) {
-  if (p.d == 128) {
-    if (p.qk_int8)
-      launch_attn_d<128, true>(p, q, ws, out, st);
-    else
-      launch_attn_d<128, false>(p, q, ws, out, st);
-  } else {
-    if (p.qk_int8)
-      launch_attn_d<64, true>(p, q, ws, out, st);
-    else
-      launch_attn_d<64, false>(p, q, ws, out, st);
-  }
+  if (p.d == 128)
+    launch_attn_m<128>(p, q, ws, out, st);
+  else
+    launch_attn_m<64>(p, q, ws, out, st);
 }
 
 void launch_debug_qk(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n, int32_t *out,

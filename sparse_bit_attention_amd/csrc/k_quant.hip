@@ -19,8 +19,9 @@ namespace sla {
 // One wave per (head, block).  Lanes 0..D/4-1 own four channels of Q for all
 // 64 rows, lanes 32..32+D/4-1 the same channels of K; each lane adds its rows
 // in order (float32).  Q's values stay in registers for the quantisation
-// (QUANT; the bf16 QK^T mode has no INT8 step).
-template <int D, bool QUANT>
+// (QUANT; the bf16 QK^T mode has no INT8 step).  FINE: one scale per 16 rows
+// (dq [blk][4]) instead of one per block.
+template <int D, bool QUANT, bool FINE>
 __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict__ Q,
                                                       const uint16_t *__restrict__ K, int N, int T,
                                                       int nblk, float *__restrict__ qbar,
@@ -41,15 +42,17 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
   const uint16_t *X = half ? K : Q;
   const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + 4 * cl;
 
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, amax = 0.f;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float ag[4] = {0.f, 0.f, 0.f, 0.f};  // amax of rows 16 g .. 16 g + 15 (all rows: ag[0])
   uint2 vals[BLK];
-  auto accum = [&](uint2 v) {
+  auto accum = [&](uint2 v, int r) {
     const float a = bf2f(v.x & 0xFFFF), b = bf2f(v.x >> 16), c = bf2f(v.y & 0xFFFF), d = bf2f(v.y >> 16);
     s0 = s0 + a;
     s1 = s1 + b;
     s2 = s2 + c;
     s3 = s3 + d;
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
+    const int gi = FINE ? (r >> 4) : 0;
+    ag[gi] = fmaxf(ag[gi], fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
   };
   if (n == BLK) {
     // full block (all but a head's last): every load is unconditional, so
@@ -60,14 +63,14 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
 #pragma unroll
     for (int r = 0; r < BLK; ++r) vals[r] = *(const uint2 *)(X + base_c + (size_t)r * D);
 #pragma unroll
-    for (int r = 0; r < BLK; ++r) accum(vals[r]);
+    for (int r = 0; r < BLK; ++r) accum(vals[r], r);
   } else {
 #pragma unroll
     for (int r = 0; r < BLK; ++r) {
       uint2 v = make_uint2(0u, 0u);
       if (act && r < n) v = *(const uint2 *)(X + base + (size_t)r * D);
       vals[r] = v;
-      if (act && r < n) accum(v);
+      if (act && r < n) accum(v, r);
     }
   }
   if (act) {
@@ -83,13 +86,19 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
     }
   }
   if constexpr (!QUANT) return;
-  // block amax of Q over lanes 0..31 (max is exact in any order)
+  // amax of Q over lanes 0..31, per block or per 16-row group (max is exact
+  // in any order)
+  constexpr int NG = FINE ? 4 : 1;
+  float inv[NG];
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  amax = __shfl(amax, 0, 64);
-  const float delta = (float)((double)amax / 127.0);
-  const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
-  if (live && l == 0) dq[blk] = delta;
+  for (int gi = 0; gi < NG; ++gi) {
+    float amax = ag[gi];
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    amax = __shfl(amax, 0, 64);
+    inv[gi] = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+    if (live && l == 0) dq[(size_t)blk * NG + gi] = (float)((double)amax / 127.0);
+  }
 
   if (half == 0 && cl < LPT) {
 #pragma unroll
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256) void k_pool_quant_q(const uint16_t *__restrict
       uint32_t packed = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float y = __builtin_rintf(x[e] * inv);
+        float y = __builtin_rintf(x[e] * inv[FINE ? (r >> 4) : 0]);
         y = fminf(fmaxf(y, -127.f), 127.f);
         packed |= ((uint32_t)(uint8_t)(int8_t)(int)y) << (8 * e);
       }
@@ -135,17 +144,24 @@ __global__ void k_kmean(const float *__restrict__ ksum, int N, int T, int D, flo
   mu[(size_t)bh * D + c] = (float)((double)s / (double)N);
 }
 
-// One wave per (head, block): k' = float32(K - mu[c]); amax over the valid rows;
-// codes = rint(k' * float32(127/amax)) clamped to [-127, 127].
-template <int D>
+// One wave per (head, block): k' = float32(K - mu[c]); amax over the valid rows
+// of the block, or (FINE) of each group of 4 rows (keys), one scale each;
+// codes = rint(k' * float32(127/amax)) clamped to [-127, 127].  dkn = the
+// largest dk_g * ||k8_s|| over the block's groups and rows (with ||q8_r|| it
+// bounds every int32 score); dkx = the largest dk_g.
+template <int D, bool FINE>
 __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
                                                  const float *__restrict__ mu, int N, int T,
                                                  int nblk, int8_t *__restrict__ k8,
-                                                 float *__restrict__ dk, float *__restrict__ dkn) {
+                                                 float *__restrict__ dk, float *__restrict__ dkn,
+                                                 float *__restrict__ dkx) {
   constexpr int LPR = D / 4;       // lanes per row
   constexpr int RPI = 64 / LPR;    // rows per step
   constexpr int STEPS = BLK / RPI;
   constexpr int KC = D / 64;
+  constexpr int NG = FINE ? 16 : 1;       // scale groups per block
+  constexpr int GS = STEPS / NG;          // steps per group
+  static_assert(GS >= 1 && STEPS % NG == 0, "a scale group is whole steps");
   __shared__ __attribute__((aligned(16))) int8_t stage[4][64 * D];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int blk = blockIdx.x * 4 + w;
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
   const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + c0;
 
   float xs[STEPS][4];
-  float amax = 0.f;
+  float as[STEPS];
   uint2 raw[STEPS];
   if (n == BLK) {
     // full block: unconditional loads, all in flight at once
@@ -180,24 +196,33 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
     xs[s][1] = bf2f(v.x >> 16) - m4.y;
     xs[s][2] = bf2f(v.y & 0xFFFF) - m4.z;
     xs[s][3] = bf2f(v.y >> 16) - m4.w;
-    if (ok)
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xs[s][0]), fabsf(xs[s][1])),
-                               fmaxf(fabsf(xs[s][2]), fabsf(xs[s][3]))));
+    as[s] = ok ? fmaxf(fmaxf(fabsf(xs[s][0]), fabsf(xs[s][1])), fmaxf(fabsf(xs[s][2]), fabsf(xs[s][3])))
+               : 0.f;
   }
+  // per group: amax over its steps and all lanes (exact in any order)
+  float inv[NG], delta[NG];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float delta = (float)((double)amax / 127.0);
-  const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
-  if (live && l == 0) dk[blk] = delta;
-  int nmax = 0;  // max over rows of the squared L2 norm of the codes
+  for (int q = 0; q < NG; ++q) {
+    float amax = 0.f;
+#pragma unroll
+    for (int s = q * GS; s < (q + 1) * GS; ++s) amax = fmaxf(amax, as[s]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    delta[q] = (float)((double)amax / 127.0);
+    inv[q] = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+    if (live && l == 0) dk[(size_t)blk * NG + q] = delta[q];
+  }
+  float bmax = 0.f, dmax = 0.f;  // the block's largest dk_g ||k8_s|| and dk_g
+  float gmax = 0.f;              // within the current group: max row ||k8_s||^2
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int r = s * RPI + r0;
+    const int q = s / GS;
     uint32_t packed = 0;
     int sq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float y = __builtin_rintf(xs[s][e] * inv);
+      float y = __builtin_rintf(xs[s][e] * inv[q]);
       y = fminf(fmaxf(y, -127.f), 127.f);
       const int code = (int)y;
       sq += code * code;
@@ -208,12 +233,20 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
     // sum over the LPR lanes holding this row
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
-    nmax = max(nmax, sq);
-  }
+    gmax = fmaxf(gmax, (float)sq);
+    if ((s + 1) % GS == 0) {
+      // the group's other rows sit in the other lanes of the step
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off, 64));
-  // dk * max_s ||k8_s||: with ||q8_r|| it bounds every int32 score of the block
-  if (live && l == 0) dkn[blk] = delta * (sqrtf((float)nmax) * (1.0f + 0x1p-20f));
+      for (int off = LPR; off < 64; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
+      bmax = fmaxf(bmax, delta[q] * (sqrtf(gmax) * (1.0f + 0x1p-20f)));
+      dmax = fmaxf(dmax, delta[q]);
+      gmax = 0.f;
+    }
+  }
+  if (live && l == 0) {
+    dkn[blk] = bmax;
+    dkx[blk] = dmax;
+  }
   __syncthreads();
   if (live) {
     const uint4 *src = (const uint4 *)stage[w];
@@ -230,7 +263,8 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K, int N, int T,
                                                   int nblk, uint16_t *__restrict__ kbf,
-                                                  float *__restrict__ dk, float *__restrict__ dkn) {
+                                                  float *__restrict__ dk, float *__restrict__ dkn,
+                                                  float *__restrict__ dkx) {
   constexpr int LPR = D / 4;       // lanes per row
   constexpr int RPI = 64 / LPR;    // rows per step
   constexpr int STEPS = BLK / RPI;
@@ -272,6 +306,7 @@ __global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K
   for (int off = LPR; off < 64; off <<= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, off, 64));
   if (live && l == 0) {
     dk[blk] = 1.0f;
+    dkx[blk] = 1.0f;
     dkn[blk] = sqrtf(nmax);
   }
   __syncthreads();
@@ -287,8 +322,11 @@ void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, co
                          hipStream_t st) {
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
-  auto kern = p.d == 128 ? (p.qk_int8 ? k_pool_quant_q<128, true> : k_pool_quant_q<128, false>)
-                         : (p.qk_int8 ? k_pool_quant_q<64, true> : k_pool_quant_q<64, false>);
+  auto kern = p.d == 128
+                  ? (p.qk_int8 ? (p.qk_fine ? k_pool_quant_q<128, true, true> : k_pool_quant_q<128, true, false>)
+                               : k_pool_quant_q<128, false, false>)
+                  : (p.qk_int8 ? (p.qk_fine ? k_pool_quant_q<64, true, true> : k_pool_quant_q<64, true, false>)
+                               : k_pool_quant_q<64, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, q, k, p.N, p.T, nblk, ws.qbar, ws.ksum, ws.kbar, ws.q8,
                      ws.dq);
 }
@@ -302,17 +340,16 @@ void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStrea
   dim3 grid((nblk + 3) / 4), block(256);
   if (!p.qk_int8) {
     if (p.d == 128)
-      hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn);
+      hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
+                         ws.dkx);
     else
-      hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn);
+      hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
+                         ws.dkx);
     return;
   }
-  if (p.d == 128)
-    hipLaunchKernelGGL(k_quant_k<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk,
-                       ws.dkn);
-  else
-    hipLaunchKernelGGL(k_quant_k<64>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk,
-                       ws.dkn);
+  auto kern = p.d == 128 ? (p.qk_fine ? k_quant_k<128, true> : k_quant_k<128, false>)
+                         : (p.qk_fine ? k_quant_k<64, true> : k_quant_k<64, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk, ws.dkn, ws.dkx);
 }
 
 }  // namespace sla

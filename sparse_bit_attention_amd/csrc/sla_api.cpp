@@ -30,6 +30,7 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.dq = (float *)(b + p.off[R_DQ]);
   w.dk = (float *)(b + p.off[R_DK]);
   w.dkn = (float *)(b + p.off[R_DKN]);
+  w.dkx = (float *)(b + p.off[R_DKX]);
   w.flags = (int32_t *)(b + p.off[R_FLAG]);
   w.maskt = (uint64_t *)(b + p.off[R_MASKT]);
   w.vt = (uint16_t *)(b + p.off[R_VT]);
@@ -75,6 +76,8 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   if (!(c.topk >= 0.0f && c.topk <= 1.0f)) return SLA_EINVAL;
   if (c.use_linear != 0 && c.use_linear != 1) return SLA_EINVAL;
   if (c.qk_int8 != 0 && c.qk_int8 != 1) return SLA_EINVAL;
+  if (c.qk_fine != 0 && c.qk_fine != 1) return SLA_EINVAL;
+  if (c.qk_fine && !c.qk_int8) return SLA_EINVAL;
   if (!(c.sm_scale >= 0.0f) || isinf(c.sm_scale)) return SLA_EINVAL;
   if (c.block != BLK) return SLA_EUNSUPPORTED;
   if (c.d != 64 && c.d != 128) return SLA_EUNSUPPORTED;
@@ -109,6 +112,7 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.rows_sel = selection_rows(c.d, p.T);
   p.lin_on = (c.use_linear == 1 && p.kb < p.T) ? 1 : 0;
   p.qk_int8 = c.qk_int8;
+  p.qk_fine = c.qk_fine;
   p.sm_scale = c.sm_scale > 0.0f ? c.sm_scale : (float)(1.0 / sqrt((double)c.d));
 
   const size_t bt = (size_t)p.BH * p.T;
@@ -121,9 +125,10 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_KEPT] = bt * (size_t)(p.kb > 0 ? p.kb : 1) * 4;
   p.size[R_Q8] = p.qk_int8 ? blk_elems : 0;
   p.size[R_K8] = p.qk_int8 ? blk_elems : 0;
-  p.size[R_DQ] = bt * 4;
-  p.size[R_DK] = bt * 4;
+  p.size[R_DQ] = bt * 4 * (p.qk_fine ? 4 : 1);
+  p.size[R_DK] = bt * 4 * (p.qk_fine ? 16 : 1);
   p.size[R_DKN] = bt * 4;
+  p.size[R_DKX] = bt * 4;
   p.size[R_FLAG] = bt * 4;
   p.size[R_MASKT] = p.lin_on ? bt * p.W64 * 8 : 0;
   p.size[R_VT] = blk_elems * 2;

@@ -23,6 +23,7 @@ enum Region {
   R_DK = SLA_WS_DK,
   R_DKN,  // f32 dk_j * max row L2 norm of the block's K8 codes   [BH][T]
           //     (bf16 QK^T: max row L2 norm of the block's K rows)
+  R_DKX,  // f32 largest K' scale of the block (bias check)       [BH][T]
   R_FLAG, // i32 query blocks left to the online-max attention    [BH][T]
   R_MASKT,// u64 mask words, word-major                          [BH][W64][T]
   R_VT,   // bf16 V per key block in kmaj_off order              [BH][T][64*d]
@@ -40,12 +41,13 @@ struct Plan {
   int rows_sel;   // query-block rows per selection workgroup
   int lin_on;     // linear branch present (use_linear and kb < T)
   int qk_int8;
+  int qk_fine;    // finer INT8 scales: 16 query rows, 4 keys per scale
   float sm_scale;
   size_t off[R_COUNT], size[R_COUNT], total;
 };
 
 struct WsPtrs {
-  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn;
+  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn, *dkx;
   uint64_t *mask, *maskt;
   int32_t *kept, *flags;
   int8_t *q8, *k8;

@@ -31,7 +31,7 @@ class sla_config(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_float),
                 ("use_linear", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("qk_int8", ctypes.c_int32)]
+                ("qk_int8", ctypes.c_int32), ("qk_fine", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,8 +92,10 @@ class PlanInfo:
 class Plan:
     """Owns an ``sla_plan_t``."""
 
-    def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True, block=64):
-        self.cfg = sla_config(B, H, N, d, block, topk, int(use_linear), sm_scale, int(qk_int8))
+    def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True, block=64,
+                 qk_fine=False):
+        self.cfg = sla_config(B, H, N, d, block, topk, int(use_linear), sm_scale, int(qk_int8),
+                              int(qk_fine))
         h = ctypes.c_void_p()
         _check(lib().sla_plan(ctypes.byref(self.cfg), ctypes.byref(h)), "sla_plan")
         self.handle = h
@@ -119,9 +121,10 @@ class SageSLA:
     """SageSLA forward on [B, H, N, d] bf16 CUDA (HIP) tensors."""
 
     def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True,
-                 device="cuda"):
+                 device="cuda", qk_fine=False):
         import torch
-        self.plan = Plan(B, H, N, d, topk, use_linear, sm_scale, qk_int8)
+        self.plan = Plan(B, H, N, d, topk, use_linear, sm_scale, qk_int8, qk_fine=qk_fine)
+        self.qk_fine = bool(qk_fine)
         self.shape = (B, H, N, d)
         self.use_linear = bool(use_linear)
         self.device = torch.device(device)
@@ -202,6 +205,8 @@ class SageSLA:
         if which == "MU":
             return raw.view(torch.float32).view(BH, d)
         if which in ("DQ", "DK"):
+            if self.qk_fine:  # one scale per 16 query rows / per 4 keys
+                return raw.view(torch.float32).view(BH, T, 4 if which == "DQ" else 16)
             return raw.view(torch.float32).view(BH, T)
         if which == "MASK":
             return raw.view(torch.int64).view(BH, T, (T + 63) // 64)

@@ -48,7 +48,8 @@ def test_status_strings():
 
 
 def plan_status(**kw):
-    cfg = dict(B=1, H=2, N=1024, d=64, block=64, topk=0.25, use_linear=1, sm_scale=0.0, qk_int8=1)
+    cfg = dict(B=1, H=2, N=1024, d=64, block=64, topk=0.25, use_linear=1, sm_scale=0.0, qk_int8=1,
+               qk_fine=0)
     cfg.update(kw)
     c = sla.sla_config(*(cfg[f] for f, _ in sla.sla_config._fields_))
     h = ctypes.c_void_p()
@@ -79,6 +80,9 @@ def plan_status(**kw):
     ({"qk_int8": 0}, sla.SLA_OK),
     ({"qk_int8": 0, "d": 128}, sla.SLA_OK),
     ({"qk_int8": 2}, sla.SLA_EINVAL),
+    ({"qk_fine": 1}, sla.SLA_OK),
+    ({"qk_fine": 1, "qk_int8": 0}, sla.SLA_EINVAL),
+    ({"qk_fine": 2}, sla.SLA_EINVAL),
 ])
 def test_plan_validation(kw, status):
     assert plan_status(**kw) == status

@@ -46,15 +46,19 @@ def f32(b):
     return synth.bf16_bits_to_f32(b).astype(np.float64)
 
 
-def run(wl: synth.Workload, inputs=None, sm_scale=0.0, out=None, qk_int8=True):
+def qk_label(qk_int8, fine):
+    return ("int8-fine" if fine else "int8") if qk_int8 else "bf16"
+
+
+def run(wl: synth.Workload, inputs=None, sm_scale=0.0, out=None, qk_int8=True, fine=False):
     if inputs is None:
         inputs = synth.all_inputs(wl)
     q, k, v, w = inputs
     Q, K, V, W = dev(q), dev(k), dev(v), dev(w)
     m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear),
-                    sm_scale=sm_scale, qk_int8=qk_int8)
+                    sm_scale=sm_scale, qk_int8=qk_int8, qk_fine=fine)
     say(f"[gpu] forward {wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} topk={wl.topk} "
-        f"lin={wl.use_linear} kb={m.plan.info.kb} qk={'int8' if qk_int8 else 'bf16'}")
+        f"lin={wl.use_linear} kb={m.plan.info.kb} qk={qk_label(qk_int8, fine)}")
     o = m(Q, K, V, W if wl.use_linear else None, out=out)
     torch.cuda.synchronize()
     return m, o, (Q, K, V, W), inputs
@@ -66,9 +70,9 @@ def unpack_mask(words, T):
     return bits.reshape(words.shape[0], -1)[:, :T]
 
 
-def check_head_prep(m, wl, b, h, Qh, Kh, qk_int8=True):
+def check_head_prep(m, wl, b, h, Qh, Kh, qk_int8=True, fine=False):
     bh = b * wl.H + h
-    prep = oracle.head_prep(Qh, Kh, float(np.float32(wl.topk)))
+    prep = oracle.head_prep(Qh, Kh, float(np.float32(wl.topk)), fine=fine)
     T, kb, d = m.plan.info.T, m.plan.info.kb, wl.d
     g = {r: m.region(r)[bh].cpu().numpy() for r in ("QBAR", "KSUM", "KBAR", "MU", "DQ", "DK")}
     assert np.array_equal(g["QBAR"].view(np.uint32), prep.qbar.view(np.uint32))
@@ -118,19 +122,19 @@ def assert_close(got, ref, label):
         assert mx == 0.0
 
 
-def full_compare(wl, sm_scale=0.0, inputs=None, qk_int8=True):
-    m, o, dv, inputs = run(wl, inputs=inputs, sm_scale=sm_scale, qk_int8=qk_int8)
+def full_compare(wl, sm_scale=0.0, inputs=None, qk_int8=True, fine=False):
+    m, o, dv, inputs = run(wl, inputs=inputs, sm_scale=sm_scale, qk_int8=qk_int8, fine=fine)
     q, k, v, w = inputs
     out = host_u16(o)
     scale = sm_scale if sm_scale > 0 else None
     G, R = [], []
     for b, h in wl.heads():
-        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h], qk_int8=qk_int8)
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h], qk_int8=qk_int8, fine=fine)
         got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep,
                                   list(range(m.plan.info.T)), sm_scale=scale, qk_int8=qk_int8)
         G.append(got)
         R.append(ref)
-    assert_close(np.concatenate(G), np.concatenate(R), wl.name + ("" if qk_int8 else " (bf16 QK)"))
+    assert_close(np.concatenate(G), np.concatenate(R), f"{wl.name} ({qk_label(qk_int8, fine)})")
     return m, o, dv, inputs
 
 
@@ -312,3 +316,76 @@ def test_sla_bf16_full_size_sampled_parity(name):
         G.append(got)
         R.append(ref)
     assert_close(np.concatenate(G), np.concatenate(R), name + " (bf16 QK)")
+
+
+# ------------------------------- fine INT8 scales (16 query rows, 4 keys) ---
+
+# The INT8 path with one Q scale per 16 rows and one K' scale per 4 keys;
+# codes, both scale arrays and the outputs against the oracle's group-scale
+# quantisers and exact branch.
+SMALL_FINE = [w for w in SMALL if w.name in (
+    "tiny", "tiny-d128-ragged", "two-blocks", "one-token", "sparse-only-b2",
+    "dense-outlier-small", "quality-topk", "sharp-online-max", "sharp-online-max-d64")]
+
+
+@pytest.mark.parametrize("wl", SMALL_FINE, ids=[w.name for w in SMALL_FINE])
+def test_fine_scales_small_full_parity(wl):
+    full_compare(wl, fine=True)
+
+
+def test_fine_scales_outlier_tokens_reduce_error():
+    """Per-group scales bound each code's step by its own group's maximum: with
+    one Q row and one K row in 64 scaled x8, the fine path lands closer to
+    float64 dense attention than the block-scale path, both run on the GPU."""
+    wl = synth.Workload("outlier-tokens", 1, 1, 2048, 128, 1.0, use_linear=0, seed=4)
+    q, k, v, w = synth.all_inputs(wl)
+    rng = np.random.default_rng(24)
+    sq, sk = np.ones((wl.N, 1)), np.ones((wl.N, 1))
+    sq[rng.choice(wl.N, wl.N // 64, replace=False)] = 8.0
+    sk[rng.choice(wl.N, wl.N // 64, replace=False)] = 8.0
+    q = q.copy()
+    k = k.copy()
+    q[0, 0] = synth.f64_to_bf16_bits(f32(q[0, 0]) * sq)
+    k[0, 0] = synth.f64_to_bf16_bits(f32(k[0, 0]) * sk)
+    exact = oracle.head_forward(q[0, 0], k[0, 0], v[0, 0], w, 1.0, use_linear=False,
+                                qk_int8=False)
+    ref = np.concatenate([exact[i] for i in range(wl.T)])
+    errs = {}
+    for fine in (False, True):
+        m, o, _, _ = run(wl, inputs=(q, k, v, w), fine=fine)
+        got = f32(host_u16(o)[0, 0])
+        errs[fine] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    say(f"[parity] outlier tokens: rel-L2 to exact, block scales {errs[False]:.3e}, "
+        f"fine scales {errs[True]:.3e}")
+    assert errs[True] < 0.75 * errs[False]
+
+
+def test_fine_int32_qk_tiles_bit_exact():
+    wl = synth.Workload("qk-fine", 1, 2, 1000, 128, 0.5, seed=2)
+    m, o, dv, (q, k, v, w) = run(wl, fine=True)
+    triples = [(0, 0, 0), (1, 15, 15), (1, 7, 2)]
+    tiles = m.debug_qk_int32(triples).cpu().numpy()
+    for n, (bh, i, j) in enumerate(triples):
+        prep = oracle.head_prep(q[0, bh], k[0, bh], float(np.float32(wl.topk)), fine=True)
+        assert np.array_equal(tiles[n], oracle.qk_int32(prep.q8, prep.k8, i, j)), (bh, i, j)
+
+
+@pytest.mark.parametrize("name", ["wan14b-720p"])
+def test_fine_full_size_sampled_parity(name):
+    wl = synth.WORKLOADS[name]
+    say(f"[gpu] generating {name}")
+    inputs = synth.all_inputs(wl)
+    m, o, dv, _ = run(wl, inputs=inputs, fine=True)
+    mask_properties(m)
+    assert bool(torch.isfinite(o.float()).all())
+    q, k, v, w = inputs
+    out = host_u16(o)
+    T = m.plan.info.T
+    blocks = sorted({0, 1, T // 2, T - 1})
+    G, R = [], []
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        prep = check_head_prep(m, wl, b, h, q[b, h], k[b, h], fine=True)
+        got, ref = compare_blocks(out[b, h], wl, q[b, h], k[b, h], v[b, h], w, prep, blocks)
+        G.append(got)
+        R.append(ref)
+    assert_close(np.concatenate(G), np.concatenate(R), name + " (int8-fine)")
