@@ -35,6 +35,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 
 TID_Q, TID_KNOISE, TID_KOFF, TID_V, TID_W, TID_OUTLIER = 1, 2, 3, 4, 5, 6
 TID_LIN_X, TID_LIN_W = 7, 8
+TID_DOUT = 9  # output gradient of the backward pass
 
 _CHUNK = 1 << 22
 
@@ -195,6 +196,13 @@ def all_inputs(wl: Workload):
             wl.seed, TID_KNOISE, per_head, e * per_head, add=offs[e * wl.d:(e + 1) * wl.d])
     v = normal_bf16(wl.seed, TID_V, n)
     return q.reshape(shape), k.reshape(shape), v.reshape(shape), proj_weight(wl)
+
+
+def grad_output(wl: Workload) -> np.ndarray:
+    """bf16 bits of the output gradient dO [B, H, N, d], N(0, 1) per element
+    (the backward pass's seeded stand-in for a training loss's gradient)."""
+    n = wl.B * wl.H * wl.N * wl.d
+    return normal_bf16(wl.seed, TID_DOUT, n).reshape(wl.B, wl.H, wl.N, wl.d)
 
 
 # ---- linear layers around attention (W8A8 GEMM inputs) ----------------------

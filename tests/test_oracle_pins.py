@@ -595,3 +595,103 @@ def test_fine_scales_reduce_int8_error():
         out = np.concatenate([res[i] for i in range(oracle.nblocks(N))])
         errs[fine] = np.linalg.norm(out - ref) / np.linalg.norm(ref)
     assert errs[True] < 0.75 * errs[False], errs
+
+
+# ---- backward of plain SLA (oracle/backward.py) ---------------------------------
+
+from oracle import backward as bwd  # noqa: E402
+
+
+def test_backward_forward_equals_c_oracle_exact_mode():
+    """The float64 forward the backward differentiates is the C oracle's
+    exact-logit (bf16 QK^T) forward, linear branch and projection included."""
+    for use_linear in (1, 0):
+        wl = synth.Workload("bwd-fwd", 1, 1, 300, 16, 0.4, use_linear=use_linear, seed=31)
+        q, k, v, w = synth.all_inputs(wl)
+        Q, K, V = q[0, 0], k[0, 0], v[0, 0]
+        prep = oracle.head_prep(Q, K, float(np.float32(wl.topk)))
+        res = oracle.head_forward(Q, K, V, w, float(np.float32(wl.topk)), use_linear=bool(use_linear),
+                                  prep=prep, qk_int8=False)
+        ref = np.concatenate([res[i] for i in range(wl.T)])
+        f = bwd.forward(f32(Q), f32(K), f32(V), f32(w), prep.mask.astype(bool),
+                        oracle.default_sm_scale(16), bool(use_linear))
+        assert np.allclose(f.O, ref, rtol=0, atol=1e-12)
+
+
+BWD_MASKS = {
+    # row 2 keeps every block (no marginal block), column 1 is kept by rows 1
+    # and 2 only
+    "mixed": [[1, 0, 1], [0, 1, 0], [1, 1, 1]],
+    # row 0 keeps nothing (linear only), row 1 everything (sparse only)
+    "extremes": [[0, 0, 0], [1, 1, 1], [0, 1, 0]],
+}
+
+
+def _bwd_problem(seed, N=150, d=8):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((N, d)) * 1.5
+    K = rng.standard_normal((N, d)) + rng.standard_normal(d)
+    V = rng.standard_normal((N, d))
+    W = rng.standard_normal((d, d)) / math.sqrt(d)
+    dO = rng.standard_normal((N, d))
+    return Q, K, V, W, dO, rng
+
+
+@pytest.mark.parametrize("mask_name", sorted(BWD_MASKS))
+@pytest.mark.parametrize("use_linear", [True, False])
+def test_backward_matches_central_differences(mask_name, use_linear):
+    """d/de sum(dO * O(X + e E)) at e = 0, by central differences of the
+    float64 forward, equals <dX, E> for random directions E in each of Q, K,
+    V, W, and single entries (ragged last block: N = 150)."""
+    Q, K, V, W, dO, rng = _bwd_problem(7 if use_linear else 8)
+    mask = np.array(BWD_MASKS[mask_name], bool)
+    sc = 0.35
+    g = bwd.backward(Q, K, V, W, dO, mask, sc, use_linear)
+
+    def loss(Q_, K_, V_, W_):
+        return float(np.sum(dO * bwd.forward(Q_, K_, V_, W_, mask, sc, use_linear).O))
+
+    args = [Q, K, V, W]
+    grads = [g.dQ, g.dK, g.dV, g.dW]
+    eps = 1e-5
+    for a in range(4):
+        dirs = [rng.standard_normal(args[a].shape)]
+        for _ in range(3):  # single entries, incl. one in the ragged block
+            E = np.zeros(args[a].shape)
+            E[tuple(rng.integers(0, n) for n in args[a].shape)] = 1.0
+            dirs.append(E)
+        if a < 3:
+            E = np.zeros(args[a].shape)
+            E[149, 3] = 1.0
+            dirs.append(E)
+        for E in dirs:
+            xp = [x.copy() for x in args]
+            xm = [x.copy() for x in args]
+            xp[a] += eps * E
+            xm[a] -= eps * E
+            fd = (loss(*xp) - loss(*xm)) / (2 * eps)
+            an = float(np.sum(grads[a] * E))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (a, fd, an)
+    if not use_linear:
+        assert np.all(g.dW == 0)
+
+
+def test_backward_euler_identities():
+    """O is linear in V (both branches) and O_l W^T is linear in W, so
+    <dV, V> = <dO, O> and <dW, W> = <dO, O_l W^T> exactly (up to rounding)."""
+    wl = synth.Workload("bwd-euler", 1, 1, 700, 32, 0.3, seed=33)
+    q, k, v, w = synth.all_inputs(wl)
+    Q, K, V, W = (f32(x) for x in (q[0, 0], k[0, 0], v[0, 0], w))
+    prep = oracle.head_prep(q[0, 0], k[0, 0], float(np.float32(wl.topk)))
+    mask = prep.mask.astype(bool)
+    dO = np.random.default_rng(3).standard_normal(Q.shape)
+    sc = oracle.default_sm_scale(32)
+    f = bwd.forward(Q, K, V, W, mask, sc, True)
+    g = bwd.backward(Q, K, V, W, dO, mask, sc, True, fwd=f)
+    assert math.isclose(np.sum(g.dV * V), np.sum(dO * f.O), rel_tol=1e-10)
+    assert math.isclose(np.sum(g.dW * W), np.sum(dO * (f.Ol @ W.T)), rel_tol=1e-10)
+    # the sparse branch is invariant to adding one vector to every key of a
+    # query block's softmax: with all blocks kept and no linear branch, dK
+    # sums to zero over the keys
+    g2 = bwd.backward(Q, K, V, W, dO, np.ones_like(mask), sc, False)
+    assert np.allclose(g2.dK.sum(axis=0), 0.0, atol=1e-10 * np.abs(g2.dK).sum())
