@@ -76,6 +76,8 @@ typedef struct {
   int32_t qk_fine;     /* INT8 scale granularity: 0 one scale per 64-row block; 1 the
                           SageAttention2++-style thread-level scales, one per 16 query
                           rows and one per 4 keys (needs qk_int8 = 1); else EINVAL */
+  int32_t backward;    /* 1: the workspace also holds what sla_attention_bwd needs
+                          (needs qk_int8 = 0, else EUNSUPPORTED); 0: forward only */
 } sla_config;
 
 typedef struct sla_plan_s *sla_plan_t;
@@ -119,6 +121,28 @@ sla_status sla_prepare_kv(sla_plan_t plan, const void *k, const void *v, const v
 sla_status sla_attend(sla_plan_t plan, const void *q, void *out, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* Backward pass of plain SLA (the trainable operator: pages "揭秘TurboDiffusion…"
+ * section "支柱二：稀疏线性注意力 – SLA" and "TurboDiffusion跨模态…" section
+ * "SLA稀疏线性注意力": the sparse pattern and the linear component are
+ * learned, so the operator is differentiated).  Gradients of sum(dout * out)
+ * with the block mask held fixed (the top-k selection passes no gradient):
+ *   sparse branch: dS = P (dP - rowsum(dout * O_sparse)), dQ = sm_scale dS K,
+ *     dK = sm_scale dS^T Q, dV = P^T dout over the kept blocks;
+ *   linear branch: through the quotient phi(Q) H_i / (phi(Q) . z_i), the
+ *     channel softmax phi, the sums H_i of the marginal key-block states and
+ *     the projection (dW = sum over all rows of dout^T O_linear).
+ * Needs a plan with backward = 1 (qk_int8 = 0) and, on the same workspace and
+ * stream, sla_quantize and sla_attention_fwd with the same q, k, v, w_proj
+ * (with backward = 1 that forward also keeps each row's softmax normaliser
+ * and the sparse-branch output in the workspace).  q, k, v, dout: bf16 [B,H,N,d];
+ * dq, dk, dv: bf16 [B,H,N,d] outputs (float32 sums, rounded once);
+ * dw: float32 [d][d] output ([d_out][d_in], summed over all heads), written
+ * (zeros when the linear branch has no marginal block); w_proj and dw may be
+ * NULL when use_linear = 0.  SLA_EUNSUPPORTED for a plan without backward. */
+sla_status sla_attention_bwd(sla_plan_t plan, const void *q, const void *k, const void *v,
+                             const void *w_proj, const void *dout, void *dq, void *dk, void *dv,
+                             float *dw, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *sla_status_string(sla_status s);
 
@@ -139,7 +163,10 @@ enum {
                       one per 16 rows)                                            */
   SLA_WS_DK = 9,   /* float [B*H][T] K' block scales (1 when qk_int8 = 0;
                       [B*H][T][16] with qk_fine: one per 4 keys)                  */
-  SLA_WS_COUNT = 10
+  SLA_WS_LSE = 10, /* float [B*H][T][64] log2 of each row's softmax normaliser in
+                      log2-scaled logit units (written by the qk_int8 = 0 forward;
+                      p = exp2(logit * sm_scale * log2(e) - lse))                 */
+  SLA_WS_COUNT = 11
 };
 
 /* Device pointer and size of one workspace region. */

@@ -17,7 +17,8 @@ OBJ = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip", "sla_api.cpp"]
+SOURCES = ["k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip", "k_bwd.hip",
+           "sla_api.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

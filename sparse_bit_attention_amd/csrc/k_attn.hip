@@ -697,7 +697,8 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
-    int32_t *__restrict__ flags, int N, int T, int kb, int nqb, int F, float qk_scale) {
+    int32_t *__restrict__ flags, float *__restrict__ lse, uint16_t *__restrict__ os, int N, int T,
+    int kb, int nqb, int F, float qk_scale) {
   constexpr int CG = D / 16, KC32 = D / 32;
   constexpr int KC = QKOps<D, QK8>::NK;
   const int lane = threadIdx.x & 63;
@@ -815,6 +816,26 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     linv[u] = 1.0f / lrow[u];
   }
 
+  // bf16 QK^T with a backward pass planned: the normalised sparse output
+  // O_sparse too (rows < N), so the backward's rowsum(dO O_sparse) does not
+  // depend on the linear branch or on the rounding of the combined output
+  if constexpr (!QK8) {
+    if (os) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = i * BLK + 16 * u + l16;
+        if (row < N) {
+          uint16_t *orow = os + ((size_t)qb * BLK + 16 * u + l16) * D;
+#pragma unroll
+          for (int a = 0; a < CG; ++a)
+            *(uint2 *)(orow + 16 * a + 4 * g) =
+                make_uint2(pack2bf(o[a][u][0] * linv[u], o[a][u][1] * linv[u]),
+                           pack2bf(o[a][u][2] * linv[u], o[a][u][3] * linv[u]));
+        }
+      }
+    }
+  }
+
   if (LIN) {
     // phi(Q) fragments: lane (query 16u + l16, group g) holds channels
     // 32kc + 8g .. +7 of its row; softmax over the row's d channels.
@@ -915,10 +936,13 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     }
   }
 
-  // store O / l: lane holds query 16u + l16, channels 16a + 4g .. +3
+  // store O / l: lane holds query 16u + l16, channels 16a + 4g .. +3.  The
+  // bf16 QK^T path also stores each row's log2 normaliser m + log2(l), so a
+  // backward pass can rebuild p = exp2(logit - lse) without the forward's max.
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row = i * BLK + 16 * u + l16;
+    if (!QK8 && g == 0 && row < N) lse[(size_t)qb * BLK + 16 * u + l16] = m[u] + log2f(lrow[u]);
     if (row < N) {
       uint16_t *orow = out + ((size_t)bh * N + row) * D;
       const float r = linv[u];
@@ -968,11 +992,11 @@ static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, ui
   const float qk_scale = p.sm_scale * LOG2E;
   const void *kfr = QK8 ? (const void *)ws.k8 : (const void *)ws.kbf;
   hipLaunchKernelGGL((k_attn<D, LIN, true, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
-                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N,
-                     p.T, p.kb, nqb, p.F, qk_scale);
+                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, ws.lse,
+                     ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale);
   hipLaunchKernelGGL((k_attn<D, LIN, false, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
-                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, p.N,
-                     p.T, p.kb, nqb, p.F, qk_scale);
+                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, ws.lse,
+                     ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale);
 }
 
 template <int D, bool QK8, bool FINE>

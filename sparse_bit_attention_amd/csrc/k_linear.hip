@@ -18,30 +18,6 @@
 
 namespace sla {
 
-typedef short v4s16 __attribute__((ext_vector_type(4)));
-
-// Four consecutive rows k0 .. k0+3 of column n0 + l%16 of a row-major bf16
-// LDS tile (pitch in elements), by the transposing LDS read: lane j of each
-// 16-lane group supplies row k0 + j/4, columns n0 + 4(j%4) .. +3.
-__device__ __forceinline__ uint2 lds_col4(const uint16_t *tile, int pitch, int k0, int n0,
-                                          int lane) {
-  const int j = lane & 15;
-  const uint16_t *a = tile + (k0 + (j >> 2)) * pitch + n0 + 4 * (j & 3);
-  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16 *)a);
-  return __builtin_bit_cast(uint2, r);
-}
-
-// MFMA operand (16x16x32 bf16, k order of kmaj_off) of the 16 columns n0 ..
-// n0+15 and the 32 keys 32 kc2 .. of a row-major [key][column] LDS tile: lane
-// (column n0 + l%16, group g = l/16) holds keys 32 kc2 + 4g + 0..3 and
-// 32 kc2 + 16 + 4g + 0..3.
-__device__ __forceinline__ v4u lds_frag(const uint16_t *tile, int pitch, int kc2, int n0, int lane) {
-  const int g = lane >> 4;
-  const uint2 lo = lds_col4(tile, pitch, 32 * kc2 + 4 * g, n0, lane);
-  const uint2 hi = lds_col4(tile, pitch, 32 * kc2 + 16 + 4 * g, n0, lane);
-  return v4u{lo.x, lo.y, hi.x, hi.y};
-}
-
 // One workgroup (4 waves) per key block.  LDS: V and phi(K) as row-major bf16
 // [key][channel] tiles; the pitch (D + 16 elements) keeps the rows 8-byte
 // aligned and puts four consecutive rows on distinct banks, so operand
@@ -452,6 +428,11 @@ void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStr
 }
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
+  launch_marginal_ptrs(p, ws.maskt, ws.hb, ws.hi, st);
+}
+
+void launch_marginal_ptrs(const Plan &p, const uint64_t *maskt, const uint16_t *hb, uint16_t *hi,
+                          hipStream_t st) {
   const int RT = (p.T + MG_BM - 1) / MG_BM, CT = (p.F + MG_BN - 1) / MG_BN;
   const int ntiles = p.BH * CT * RT;
   // persistent: one workgroup per CU (256 CUs, 8 XCDs), fewer for small
@@ -459,9 +440,9 @@ void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   const int nwg = std::min(256, 8 * ((ntiles + 7) / 8));
   dim3 grid(nwg), block(512);
   if (p.d == 128)
-    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ntiles, ws.hi);
+    hipLaunchKernelGGL(k_marginal<128>, grid, block, 0, st, maskt, hb, p.T, p.W64, p.F, ntiles, hi);
   else
-    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, ws.maskt, ws.hb, p.T, p.W64, p.F, ntiles, ws.hi);
+    hipLaunchKernelGGL(k_marginal<64>, grid, block, 0, st, maskt, hb, p.T, p.W64, p.F, ntiles, hi);
 }
 
 }  // namespace sla

@@ -38,6 +38,15 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.wsw = (uint16_t *)(b + p.off[R_WSW]);
   w.hb = (uint16_t *)(b + p.off[R_HB]);
   w.hi = (uint16_t *)(b + p.off[R_HI]);
+  w.lse = (float *)(b + p.off[R_LSE]);
+  w.mt = (uint64_t *)(b + p.off[R_MT]);
+  w.mtt = (uint64_t *)(b + p.off[R_MTT]);
+  w.delta = (float *)(b + p.off[R_DELTA]);
+  w.ol = (uint16_t *)(b + p.off[R_OL]);
+  w.dhi = (uint16_t *)(b + p.off[R_DHI]);
+  w.dhb = (uint16_t *)(b + p.off[R_DHB]);
+  w.dwp = (float *)(b + p.off[R_DWP]);
+  w.os = p.size[R_OS] ? (uint16_t *)(b + p.off[R_OS]) : nullptr;
   return w;
 }
 
@@ -78,6 +87,8 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   if (c.qk_int8 != 0 && c.qk_int8 != 1) return SLA_EINVAL;
   if (c.qk_fine != 0 && c.qk_fine != 1) return SLA_EINVAL;
   if (c.qk_fine && !c.qk_int8) return SLA_EINVAL;
+  if (c.backward != 0 && c.backward != 1) return SLA_EINVAL;
+  if (c.backward && c.qk_int8) return SLA_EUNSUPPORTED;  // the backward is plain SLA's
   if (!(c.sm_scale >= 0.0f) || isinf(c.sm_scale)) return SLA_EINVAL;
   if (c.block != BLK) return SLA_EUNSUPPORTED;
   if (c.d != 64 && c.d != 128) return SLA_EUNSUPPORTED;
@@ -113,6 +124,8 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.lin_on = (c.use_linear == 1 && p.kb < p.T) ? 1 : 0;
   p.qk_int8 = c.qk_int8;
   p.qk_fine = c.qk_fine;
+  p.bwd = c.backward;
+  p.dw_chunks = (p.BH * p.T + DW_CHUNK - 1) / DW_CHUNK;
   p.sm_scale = c.sm_scale > 0.0f ? c.sm_scale : (float)(1.0 / sqrt((double)c.d));
 
   const size_t bt = (size_t)p.BH * p.T;
@@ -136,6 +149,15 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_WSW] = p.lin_on ? (size_t)p.d * p.d * 2 : 0;
   p.size[R_HB] = p.lin_on ? bt * p.F * 2 : 0;
   p.size[R_HI] = p.lin_on ? bt * p.F * 2 : 0;
+  p.size[R_LSE] = bt * BLK * 4;
+  p.size[R_MT] = p.bwd ? bt * p.W64 * 8 : 0;
+  p.size[R_MTT] = p.bwd && p.lin_on ? bt * p.W64 * 8 : 0;
+  p.size[R_DELTA] = p.bwd ? bt * BLK * 4 : 0;
+  p.size[R_OS] = p.bwd ? blk_elems * 2 : 0;
+  p.size[R_OL] = p.bwd && p.lin_on ? blk_elems * 2 : 0;
+  p.size[R_DHI] = p.bwd && p.lin_on ? bt * p.F * 2 : 0;
+  p.size[R_DHB] = p.bwd && p.lin_on ? bt * p.F * 2 : 0;
+  p.size[R_DWP] = p.bwd && p.lin_on ? (size_t)p.dw_chunks * p.d * p.d * 4 : 0;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
     p.off[r] = o;
@@ -254,6 +276,28 @@ sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *de
   (void)hipGetLastError();
   WsPtrs w = ws_ptrs(p, (void *)ws);
   launch_debug_qk(p, w, dev_pairs, n, dev_out, (hipStream_t)stream);
+  return launched();
+}
+
+sla_status sla_attention_bwd(sla_plan_t plan, const void *q, const void *k, const void *v,
+                             const void *w_proj, const void *dout, void *dq, void *dk, void *dv,
+                             float *dw, void *ws, size_t ws_bytes, void *stream) {
+  if (!plan || !q || !k || !v || !dout || !dq || !dk || !dv) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (!p.bwd) return SLA_EUNSUPPORTED;
+  if (p.cfg.use_linear && (!w_proj || !dw)) return SLA_EINVAL;
+  const void *a16[] = {q, k, v, dout, dq, dk, dv};
+  for (const void *x : a16)
+    if (!aligned(x, 16)) return SLA_EINVAL;
+  if (w_proj && !aligned(w_proj, 16)) return SLA_EINVAL;
+  if (dw && !aligned(dw, 4)) return SLA_EINVAL;
+  sla_status s = check_ws(p, ws, ws_bytes);
+  if (s != SLA_OK) return s;
+  (void)hipGetLastError();
+  launch_bwd(p, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
+             (const uint16_t *)w_proj, (const uint16_t *)dout,
+             (uint16_t *)dq, (uint16_t *)dk, (uint16_t *)dv, p.cfg.use_linear ? dw : nullptr,
+             ws_ptrs(p, ws), (hipStream_t)stream);
   return launched();
 }
 

@@ -106,6 +106,44 @@ __host__ __device__ __forceinline__ int hstate_off(int c, int c2, int KC32) {
   return (((c2 >> 4) * KC32 + (c >> 5)) * 64 + (c2 & 15) + 16 * ((c & 31) >> 3)) * 8 + (c & 7);
 }
 
+// ---------------------------------------------------------------------------
+// LDS operand reads (row-major bf16 tiles)
+// ---------------------------------------------------------------------------
+
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+
+// Four consecutive rows k0 .. k0+3 of column n0 + l%16 of a row-major bf16
+// LDS tile (pitch in elements), by the transposing LDS read: lane j of each
+// 16-lane group supplies row k0 + j/4, columns n0 + 4(j%4) .. +3.
+__device__ __forceinline__ uint2 lds_col4(const uint16_t *tile, int pitch, int k0, int n0,
+                                          int lane) {
+  const int j = lane & 15;
+  const uint16_t *a = tile + (k0 + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16 *)a);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// MFMA operand (16x16x32 bf16, k order of kmaj_off) of the 16 columns n0 ..
+// n0+15 and the 32 keys 32 kc2 .. of a row-major [key][column] LDS tile: lane
+// (column n0 + l%16, group g = l/16) holds keys 32 kc2 + 4g + 0..3 and
+// 32 kc2 + 16 + 4g + 0..3.
+__device__ __forceinline__ v4u lds_frag(const uint16_t *tile, int pitch, int kc2, int n0, int lane) {
+  const int g = lane >> 4;
+  const uint2 lo = lds_col4(tile, pitch, 32 * kc2 + 4 * g, n0, lane);
+  const uint2 hi = lds_col4(tile, pitch, 32 * kc2 + 16 + 4 * g, n0, lane);
+  return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
+// MFMA operand (16x16x32 bf16) of the 16 rows r0 .. r0+15 of a row-major
+// [row][k] LDS tile, in the same k order as lds_frag: lane (row r0 + l%16,
+// group g) holds k = 32 kc + 4g + 0..3 and 32 kc + 16 + 4g + 0..3.
+__device__ __forceinline__ v4u lds_rows(const uint16_t *tile, int pitch, int r0, int kc, int lane) {
+  const uint16_t *a = tile + (r0 + (lane & 15)) * pitch + 32 * kc + 4 * (lane >> 4);
+  const uint2 lo = *(const uint2 *)a;
+  const uint2 hi = *(const uint2 *)(a + 16);
+  return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
 // Workgroup id -> logical id so that consecutive logical ids share an XCD
 // (workgroups are dispatched round robin over the 8 XCDs).
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {

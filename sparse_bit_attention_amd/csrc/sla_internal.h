@@ -21,6 +21,7 @@ enum Region {
   R_K8 = SLA_WS_K8,
   R_DQ = SLA_WS_DQ,
   R_DK = SLA_WS_DK,
+  R_LSE = SLA_WS_LSE,
   R_DKN,  // f32 dk_j * max row L2 norm of the block's K8 codes   [BH][T]
           //     (bf16 QK^T: max row L2 norm of the block's K rows)
   R_DKX,  // f32 largest K' scale of the block (bias check)       [BH][T]
@@ -31,6 +32,15 @@ enum Region {
   R_WSW,  // bf16 projection in wfrag_off order                  [d*d]
   R_HB,   // bf16 per key block linear state (hstate_off order)  [BH][T][F]
   R_HI,   // bf16 per query block marginal state (same order)    [BH][T][F]
+  // backward pass (plans with backward = 1)
+  R_MT,   // u64 transposed mask, row j = key block, bits = query blocks [BH][T][W64]
+  R_MTT,  // u64 the same, word-major (marginal GEMM operand)    [BH][W64][T]
+  R_DELTA,// f32 rowsum(dO * O_sparse)                           [BH][T][64]
+  R_OS,   // bf16 sparse-branch output O_sparse (forward)         [BH][T][64][d]
+  R_OL,   // bf16 linear-branch rows O_l before the projection   [BH][T][64][d]
+  R_DHI,  // bf16 gradient of the marginal state (dh_off order)  [BH][T][F]
+  R_DHB,  // bf16 gradient of the key-block state (same order)   [BH][T][F]
+  R_DWP,  // f32 partial projection gradients                    [nchunk][d][d]
   R_COUNT
 };
 
@@ -42,12 +52,16 @@ struct Plan {
   int lin_on;     // linear branch present (use_linear and kb < T)
   int qk_int8;
   int qk_fine;    // finer INT8 scales: 16 query rows, 4 keys per scale
+  int bwd;        // workspace holds the backward regions
+  int dw_chunks;  // query blocks are summed into dW partials in chunks of DW_CHUNK
   float sm_scale;
   size_t off[R_COUNT], size[R_COUNT], total;
 };
 
 struct WsPtrs {
-  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn, *dkx;
+  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn, *dkx, *lse, *delta, *dwp;
+  uint64_t *mt, *mtt;
+  uint16_t *ol, *dhi, *dhb, *os;
   uint64_t *mask, *maskt;
   int32_t *kept, *flags;
   int8_t *q8, *k8;
@@ -65,9 +79,18 @@ void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const W
                     hipStream_t st);
 void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st);
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st);
+// H = (1 - M) Hb per head for a word-major mask (the forward's M, or its
+// transpose for the backward's dHb = (1 - M)^T dH)
+void launch_marginal_ptrs(const Plan &p, const uint64_t *maskt, const uint16_t *hb, uint16_t *hi,
+                          hipStream_t st);
 void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out, hipStream_t st);
 void launch_debug_qk(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n, int32_t *out,
                      hipStream_t st);
+// backward pass of plain SLA
+constexpr int DW_CHUNK = 64;  // query blocks per dW partial
+void launch_bwd(const Plan &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const uint16_t *w, const uint16_t *dout, uint16_t *dq,
+                uint16_t *dk, uint16_t *dv, float *dw, const WsPtrs &ws, hipStream_t st);
 void launch_quant_b128(const uint16_t *x, int R, int C, int8_t *codes, float *scales,
                        hipStream_t st);
 void launch_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw, int M,

@@ -14,11 +14,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsagesla.so")
 
 SLA_OK, SLA_EINVAL, SLA_EUNSUPPORTED, SLA_EWORKSPACE, SLA_EHIP, SLA_ENOMEM = range(6)
-WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "DK"]
+WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "DK", "LSE"]
 
 EXPORTS = ["sla_plan", "sla_plan_destroy", "sla_plan_info", "sla_quantize", "sla_attention_fwd",
            "sla_prepare_kv", "sla_attend", "sla_status_string", "sla_ws_view",
-           "sla_debug_qk_int32", "sla_quant_b128", "sla_w8a8_gemm"]
+           "sla_debug_qk_int32", "sla_quant_b128", "sla_w8a8_gemm", "sla_attention_bwd"]
 
 
 class SlaError(RuntimeError):
@@ -31,7 +31,8 @@ class sla_config(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_float),
                 ("use_linear", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("qk_int8", ctypes.c_int32), ("qk_fine", ctypes.c_int32)]
+                ("qk_int8", ctypes.c_int32), ("qk_fine", ctypes.c_int32),
+                ("backward", ctypes.c_int32)]
 
 
 _lib = None
@@ -69,6 +70,8 @@ def lib():
         L.sla_quant_b128.restype = ctypes.c_int
         L.sla_w8a8_gemm.argtypes = [P, P, P, P, i32, i32, i32, P, P]
         L.sla_w8a8_gemm.restype = ctypes.c_int
+        L.sla_attention_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.sla_attention_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -93,9 +96,9 @@ class Plan:
     """Owns an ``sla_plan_t``."""
 
     def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True, block=64,
-                 qk_fine=False):
+                 qk_fine=False, backward=False):
         self.cfg = sla_config(B, H, N, d, block, topk, int(use_linear), sm_scale, int(qk_int8),
-                              int(qk_fine))
+                              int(qk_fine), int(backward))
         h = ctypes.c_void_p()
         _check(lib().sla_plan(ctypes.byref(self.cfg), ctypes.byref(h)), "sla_plan")
         self.handle = h
@@ -118,12 +121,14 @@ class Plan:
 
 
 class SageSLA:
-    """SageSLA forward on [B, H, N, d] bf16 CUDA (HIP) tensors."""
+    """SageSLA forward (and, for plain SLA with backward=True, its backward) on
+    [B, H, N, d] bf16 CUDA (HIP) tensors."""
 
     def __init__(self, B, H, N, d, topk, use_linear=True, sm_scale=0.0, qk_int8=True,
-                 device="cuda", qk_fine=False):
+                 device="cuda", qk_fine=False, backward=False):
         import torch
-        self.plan = Plan(B, H, N, d, topk, use_linear, sm_scale, qk_int8, qk_fine=qk_fine)
+        self.plan = Plan(B, H, N, d, topk, use_linear, sm_scale, qk_int8, qk_fine=qk_fine,
+                         backward=backward)
         self.qk_fine = bool(qk_fine)
         self.shape = (B, H, N, d)
         self.use_linear = bool(use_linear)
@@ -191,6 +196,31 @@ class SageSLA:
 
     __call__ = forward
 
+    def backward(self, q, k, v, w, dout, dq=None, dk=None, dv=None, dw=None, stream=None):
+        """Gradients (dq, dk, dv bf16 [B,H,N,d]; dw float32 [d,d] or None) of
+        sum(dout * out) after forward() on the same inputs (plain SLA)."""
+        import torch
+        d = self.shape[3]
+
+        def new(x):
+            return x if x is not None else torch.empty(self.shape, dtype=torch.bfloat16,
+                                                       device=self.device)
+        dq, dk, dv = new(dq), new(dk), new(dv)
+        if self.use_linear and dw is None:
+            dw = torch.empty((d, d), dtype=torch.float32, device=self.device)
+        if dw is not None and (dw.dtype != torch.float32 or tuple(dw.shape) != (d, d)
+                               or not dw.is_contiguous()):
+            raise ValueError("dw must be a contiguous float32 [d, d] device tensor")
+        wp = self._tensor(w, "w", (d, d)) if w is not None else ctypes.c_void_p(0)
+        _check(lib().sla_attention_bwd(
+            self.plan.handle, self._tensor(q, "q", self.shape), self._tensor(k, "k", self.shape),
+            self._tensor(v, "v", self.shape), wp, self._tensor(dout, "dout", self.shape), self._tensor(dq, "dq", self.shape),
+            self._tensor(dk, "dk", self.shape), self._tensor(dv, "dv", self.shape),
+            ctypes.c_void_p(dw.data_ptr() if dw is not None else 0),
+            ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), self._stream(stream)),
+            "sla_attention_bwd")
+        return dq, dk, dv, dw
+
     # -- debug views -----------------------------------------------------------
     def region(self, which: str):
         """A torch view of one workspace region (see sagesla.h)."""
@@ -214,6 +244,8 @@ class SageSLA:
             return raw.view(torch.int32).view(BH, T, max(kb, 1))[:, :, :kb]
         if which in ("Q8", "K8"):
             return raw.view(torch.int8).view(BH, T, 64 * d)
+        if which == "LSE":
+            return raw.view(torch.float32).view(BH, T, 64)
         raise KeyError(which)
 
     def debug_qk_int32(self, triples, stream=None):

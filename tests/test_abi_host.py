@@ -49,7 +49,7 @@ def test_status_strings():
 
 def plan_status(**kw):
     cfg = dict(B=1, H=2, N=1024, d=64, block=64, topk=0.25, use_linear=1, sm_scale=0.0, qk_int8=1,
-               qk_fine=0)
+               qk_fine=0, backward=0)
     cfg.update(kw)
     c = sla.sla_config(*(cfg[f] for f, _ in sla.sla_config._fields_))
     h = ctypes.c_void_p()
@@ -83,6 +83,10 @@ def plan_status(**kw):
     ({"qk_fine": 1}, sla.SLA_OK),
     ({"qk_fine": 1, "qk_int8": 0}, sla.SLA_EINVAL),
     ({"qk_fine": 2}, sla.SLA_EINVAL),
+    ({"backward": 1, "qk_int8": 0}, sla.SLA_OK),
+    ({"backward": 1, "qk_int8": 0, "use_linear": 0}, sla.SLA_OK),
+    ({"backward": 1}, sla.SLA_EUNSUPPORTED),  # the backward is plain SLA's
+    ({"backward": 2, "qk_int8": 0}, sla.SLA_EINVAL),
 ])
 def test_plan_validation(kw, status):
     assert plan_status(**kw) == status
@@ -182,3 +186,38 @@ def test_w8a8_argument_checks_without_gpu():
     assert L.sla_quant_b128(a, 4, 20, a, a, None) == sla.SLA_EUNSUPPORTED
     assert L.sla_quant_b128(a, 0, 16, a, a, None) == sla.SLA_EINVAL
     assert L.sla_quant_b128(None, 4, 16, a, a, None) == sla.SLA_EINVAL
+
+
+def test_backward_workspace_and_argument_checks():
+    """Backward plans add the transposed mask, rowsum(dO O), O_l, the two
+    state-gradient arrays and the dW partials; forward-only plans refuse the
+    backward call; bad arguments are refused on the host."""
+    B, H, N, d = 1, 40, 75600, 128
+    pf = sla.Plan(B, H, N, d, 0.1, qk_int8=False)
+    pb = sla.Plan(B, H, N, d, 0.1, qk_int8=False, backward=True)
+    T = pb.info.T
+    BH = B * H
+    F = (d * d + d + 127) // 128 * 128
+    grow = pb.info.workspace_bytes - pf.info.workspace_bytes
+    expect = (2 * BH * T * math.ceil(T / 64) * 8 + BH * T * 64 * 4 + 2 * BH * T * 64 * d * 2
+              + 2 * BH * T * F * 2 + math.ceil(BH * T / 64) * d * d * 4)
+    assert 0 <= grow - expect <= 8 * 256
+    assert pb.ws_region(0, "LSE")[1] == BH * T * 64 * 4
+    L = sla.lib()
+    fake = ctypes.c_void_p(1 << 40)  # never dereferenced: validation fails first
+    big = pb.info.workspace_bytes
+    args = [fake] * 9
+    assert L.sla_attention_bwd(pf.handle, *args, fake, pf.info.workspace_bytes, None) == sla.SLA_EUNSUPPORTED
+    assert L.sla_attention_bwd(pb.handle, *args, fake, big - 1, None) == sla.SLA_EWORKSPACE
+    for k in range(9):
+        a = list(args)
+        if k in (3, 8):  # w_proj, dw: required while the linear branch is on
+            a[k] = None
+            assert L.sla_attention_bwd(pb.handle, *a, fake, big, None) == sla.SLA_EINVAL, k
+            continue
+        a[k] = None
+        assert L.sla_attention_bwd(pb.handle, *a, fake, big, None) == sla.SLA_EINVAL, k
+        a[k] = ctypes.c_void_p((1 << 40) + 8)
+        assert L.sla_attention_bwd(pb.handle, *a, fake, big, None) == sla.SLA_EINVAL, k
+    pn = sla.Plan(1, 2, 1000, 64, 0.3, use_linear=False, qk_int8=False, backward=True)
+    assert pn.ws_region(0, "LSE")[1] == 2 * 16 * 64 * 4
