@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan14b-720p]
                     [--qk int8|int8-fine|bf16]
     python bench.py --op w8a8 [--linear wan14b-720p-qkv]   (the W8A8 linear layer)
+    python bench.py --op bwd [--workload wan14b-720p]      (plain-SLA backward)
 
 One step = the whole forward (sla_quantize, then sla_prepare_kv and
 sla_attend) over one batch of seeded synthetic inputs already resident in
@@ -188,6 +189,92 @@ def bench_w8a8(args, dev):
     print(json.dumps(res), flush=True)
 
 
+def bwd_work(wl, T, kb):
+    """MFMA flops the backward kernels execute per call (bf16): per kept pair
+    seven 64x64xd products (S, dP and dQ in the query-block kernel; S, dP,
+    dV and dK in the key-block kernel); with the linear branch, per query
+    block four 64xdxd products (phi(Q) H, dO W, dnum H^T, phi(Q)^T dnum) plus
+    one for dW, per key block two (dHb^T phi(K), dHb V), and per head the
+    transposed marginal GEMM 2 T^2 F."""
+    BH = wl.B * wl.H
+    pairs = BH * T * kb
+    flops = pairs * 7 * 2 * 64 * 64 * wl.d
+    if wl.use_linear and kb < T:
+        F = (wl.d * wl.d + wl.d + 127) // 128 * 128
+        flops += BH * T * (5 + 2) * 2 * 64 * wl.d * wl.d + BH * 2.0 * T * T * F
+    return flops
+
+
+def bench_bwd(args, dev):
+    """One step = the plain-SLA training pair on one batch: the forward of a
+    backward plan (sla_quantize, sla_attention_fwd; bf16 QK^T) then
+    sla_attention_bwd with a seeded output gradient.  value = backward
+    dense-equivalent TFLOP/s (the FlashAttention convention: 2.5 x the
+    forward's 4 B H N^2 d); the roofline is the whole backward call's
+    executed MFMA flops against the dense bf16 peak."""
+    import torch
+    from sparse_bit_attention_amd import sla
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {wl.name} inputs and the output gradient")
+    q, k, v, w = synth.all_inputs(wl)
+    do = synth.grad_output(wl)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V, W, dO = up(q), up(k), up(v), up(w), up(do)
+    del q, k, v, do
+    m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear), device=dev,
+                    qk_int8=False, backward=True)
+    T, kb = m.plan.info.T, m.plan.info.kb
+    Wp = W if wl.use_linear else None
+    out = torch.empty_like(Q)
+    dq, dk, dv = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    dw = torch.empty((wl.d, wl.d), dtype=torch.float32, device=dev) if wl.use_linear else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m.quantize(Q, K, stream)
+        m.attention(Q, K, V, Wp, out, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        m.backward(Q, K, V, Wp, dO, dq, dk, dv, dw, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    log(f"[bench] ms/step {ms_step:.3f} (forward {f_ms:.3f}, backward {b_ms:.3f})")
+    dense = 10.0 * wl.B * wl.H * wl.N * wl.N * wl.d
+    flops = bwd_work(wl, T, kb)
+    res = {
+        "metric": "SLA backward (bf16 QK^T, block mask fixed), dense-equivalent TFLOP/s",
+        "value": dense / (b_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent, 10 B H N^2 d per backward)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "block": 64,
+                   "topk": wl.topk, "kb": kb, "use_linear": wl.use_linear},
+        "stage_ms": {"forward (sla_quantize + sla_attention_fwd)": f_ms, "sla_attention_bwd": b_ms},
+        "roofline": {"kernel": "sla_attention_bwd (all backward kernels)", "bound": "mfma",
+                     "achieved": flops / (b_ms * 1e-3) / 1e12, "peak": P_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": flops / (b_ms * 1e-3) / P_BF16, "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,8 +287,9 @@ def main():
                     help="QK^T operands: int8 (SageSLA with one scale per 64-row block, the "
                          "default), int8-fine (one Q scale per 16 rows, one K scale per 4 "
                          "keys) or bf16 (plain SLA)")
-    ap.add_argument("--op", choices=("sagesla", "w8a8"), default="sagesla",
-                    help="sagesla: the attention forward (default); w8a8: the W8A8 linear layer")
+    ap.add_argument("--op", choices=("sagesla", "w8a8", "bwd"), default="sagesla",
+                    help="sagesla: the attention forward (default); w8a8: the W8A8 linear layer; "
+                         "bwd: plain-SLA forward + backward (training pair)")
     ap.add_argument("--linear", default="wan14b-720p-qkv", choices=sorted(synth.LINEAR_WORKLOADS))
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -232,6 +320,9 @@ def main():
 
     if args.op == "w8a8":
         bench_w8a8(args, dev)
+        return
+    if args.op == "bwd":
+        bench_bwd(args, dev)
         return
 
     wl = synth.WORKLOADS[args.workload]

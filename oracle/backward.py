@@ -181,3 +181,91 @@ def head_backward(Q, K, V, W, dO, mask, sm_scale, use_linear=True):
 def _bf16_to_f64(b):
     b = np.ascontiguousarray(b, np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _block_states(K, V, T):
+    """Hb [T, d, d] and zb [T, d]: phi(K_j)^T V_j and phi(K_j)^T 1 per key block."""
+    N, d = K.shape
+    Hb = np.zeros((T, d, d))
+    zb = np.zeros((T, d))
+    for j in range(T):
+        B = phi(K[_rows(j, N)])
+        Hb[j] = B.T @ V[_rows(j, N)]
+        zb[j] = B.sum(axis=0)
+    return Hb, zb
+
+
+def backward_sampled(Q, K, V, W, dO, mask, sm_scale, qblocks, kblocks, use_linear=True):
+    """The same gradients as ``backward`` restricted to the rows of the query
+    blocks ``qblocks`` (dQ) and the key blocks ``kblocks`` (dK, dV), plus the
+    whole dW, for heads too large for ``backward``.  The marginal sums
+    H_i = sum over marginal j of Hb_j (and their transposes for dHb_j) are
+    written as one matrix product with the complement mask.
+    Returns ({i: dQ rows}, {j: dK rows}, {j: dV rows}, dW)."""
+    N, d = Q.shape
+    T = mask.shape[0]
+    comp = (~mask).astype(np.float64)
+    dQ = {i: np.zeros((min(BLOCK, N - BLOCK * i), d)) for i in qblocks}
+    dK = {j: np.zeros((min(BLOCK, N - BLOCK * j), d)) for j in kblocks}
+    dV = {j: np.zeros((min(BLOCK, N - BLOCK * j), d)) for j in kblocks}
+    dW = np.zeros((d, d))
+
+    def sparse_rows(i):
+        """P, dS and the key rows of query block i's softmax."""
+        r = _rows(i, N)
+        s = _key_rows(np.flatnonzero(mask[i]), N)
+        L = Q[r] @ K[s].T * sm_scale
+        m = L.max(axis=1, keepdims=True)
+        E = np.exp(L - m)
+        P = E / E.sum(axis=1, keepdims=True)
+        Os = P @ V[s]
+        dP = dO[r] @ V[s].T
+        D = (dO[r] * Os).sum(axis=1, keepdims=True)
+        return s, P, P * (dP - D)
+
+    for i in qblocks:
+        if mask[i].any():
+            s, P, dS = sparse_rows(i)
+            dQ[i] += sm_scale * dS @ K[s]
+    users = sorted({int(i) for j in kblocks for i in np.flatnonzero(mask[:, j])})
+    for i in users:
+        s, P, dS = sparse_rows(i)
+        r = _rows(i, N)
+        for j in kblocks:
+            if not mask[i, j]:
+                continue
+            # positions of key block j's rows inside s
+            pos = np.flatnonzero((s >= BLOCK * j) & (s < BLOCK * j + dK[j].shape[0]))
+            dK[j] += sm_scale * dS[:, pos].T @ Q[r]
+            dV[j] += P[:, pos].T @ dO[r]
+
+    if use_linear:
+        Hb, zb = _block_states(K, V, T)
+        H = (comp @ Hb.reshape(T, d * d)).reshape(T, d, d)
+        z = comp @ zb
+        G = dO @ W
+        dH = np.zeros((T, d, d))
+        dz = np.zeros((T, d))
+        for i in range(T):
+            if not comp[i].any():
+                continue
+            r = _rows(i, N)
+            A = phi(Q[r])
+            den = (A @ z[i])[:, None]
+            Ol = (A @ H[i]) / den
+            dW += dO[r].T @ Ol
+            dnum = G[r] / den
+            dden = -(G[r] * Ol).sum(axis=1, keepdims=True) / den
+            dH[i] = A.T @ dnum
+            dz[i] = (A * dden).sum(axis=0)
+            if i in dQ:
+                dA = dnum @ H[i].T + dden * z[i][None, :]
+                dQ[i] += phi_grad(A, dA)
+        dHb = (comp.T @ dH.reshape(T, d * d)).reshape(T, d, d)
+        dzb = comp.T @ dz
+        for j in kblocks:
+            rj = _rows(j, N)
+            B = phi(K[rj])
+            dV[j] += B @ dHb[j]
+            dK[j] += phi_grad(B, V[rj] @ dHb[j].T + dzb[j][None, :])
+    return dQ, dK, dV, dW

@@ -184,3 +184,57 @@ def test_backward_needs_backward_plan():
     o = m(Q, K, V, W)
     with pytest.raises(sla.SlaError):
         m.backward(Q, K, V, W, o)
+
+
+# ---------------------------------------------------------------- full size ---
+
+def sampled_compare(wl, heads, check_dw):
+    say(f"[gpu] generating {wl.name}")
+    m, (q, k, v, w, do), o, (dq, dk, dv, dw) = run_bwd(wl)
+    T = m.plan.info.T
+    sc = oracle.default_sm_scale(wl.d)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    qbl = sorted({0, 1, T // 2, T - 1})
+    kbl = sorted({0, T // 2, T - 1})
+    masks = unpack_mask(m.region("MASK").cpu().numpy().reshape(wl.B * wl.H * T, -1), T)
+    G = {"dQ": [], "dK": [], "dV": []}
+    R = {"dQ": [], "dK": [], "dV": []}
+    dW = np.zeros((wl.d, wl.d))
+    for b, h in heads:
+        bh = b * wl.H + h
+        mask = masks[bh * T:(bh + 1) * T].astype(bool)
+        rq, rk, rv, rw = obwd.backward_sampled(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(w),
+                                               f64(do[b, h]), mask, sc, qbl, kbl,
+                                               bool(wl.use_linear))
+        dW += rw
+        hq = dq[b, h]
+        for i in qbl:
+            n = rq[i].shape[0]
+            G["dQ"].append(host_f64(hq[64 * i:64 * i + n]))
+            R["dQ"].append(rq[i])
+        for j in kbl:
+            n = rk[j].shape[0]
+            G["dK"].append(host_f64(dk[b, h, 64 * j:64 * j + n]))
+            R["dK"].append(rk[j])
+            G["dV"].append(host_f64(dv[b, h, 64 * j:64 * j + n]))
+            R["dV"].append(rv[j])
+    for name in ("dQ", "dK", "dV"):
+        close(np.concatenate(G[name]), np.concatenate(R[name]), f"{wl.name} {name} (sampled)")
+    if check_dw:
+        close(host_f64(dw), dW, f"{wl.name} dW")
+
+
+def test_backward_wan14b_720p_sampled():
+    """The Wan2.1-14B 720P layer (40 heads, N = 75600, topk 0.1) in the launch
+    configuration the backward benchmark times; dQ rows of four query blocks
+    and dK, dV rows of three key blocks (first, middle, ragged last) on two heads."""
+    wl = synth.WORKLOADS["wan14b-720p"]
+    sampled_compare(wl, [(0, 0), (0, wl.H - 1)], check_dw=False)
+
+
+def test_backward_full_length_two_heads_dw():
+    """Full 720P sequence length with two heads, so the oracle can also form
+    the whole projection gradient (a sum over every row of every head)."""
+    wl = synth.Workload("wan14b-720p-h2", 1, 2, 21 * 45 * 80, 128, 0.1)
+    sampled_compare(wl, wl.heads(), check_dw=True)

@@ -695,3 +695,24 @@ def test_backward_euler_identities():
     # sums to zero over the keys
     g2 = bwd.backward(Q, K, V, W, dO, np.ones_like(mask), sc, False)
     assert np.allclose(g2.dK.sum(axis=0), 0.0, atol=1e-10 * np.abs(g2.dK).sum())
+
+
+@pytest.mark.parametrize("use_linear", [True, False])
+def test_backward_sampled_equals_full(use_linear):
+    """The sampled form (for full-size heads) gives the full backward's rows."""
+    wl = synth.Workload("bwd-samp", 1, 1, 1000, 32, 0.25, seed=34)
+    q, k, v, w = synth.all_inputs(wl)
+    Q, K, V, W = (f32(x) for x in (q[0, 0], k[0, 0], v[0, 0], w))
+    prep = oracle.head_prep(q[0, 0], k[0, 0], float(np.float32(wl.topk)))
+    mask = prep.mask.astype(bool)
+    dO = np.random.default_rng(5).standard_normal(Q.shape)
+    sc = oracle.default_sm_scale(32)
+    g = bwd.backward(Q, K, V, W, dO, mask, sc, use_linear)
+    qb, kb_ = [0, 7, 15], [1, 15]
+    dQ, dK, dV, dW = bwd.backward_sampled(Q, K, V, W, dO, mask, sc, qb, kb_, use_linear)
+    for i in qb:
+        assert np.allclose(dQ[i], g.dQ[64 * i:64 * i + dQ[i].shape[0]], rtol=0, atol=1e-12)
+    for j in kb_:
+        assert np.allclose(dK[j], g.dK[64 * j:64 * j + dK[j].shape[0]], rtol=0, atol=1e-12)
+        assert np.allclose(dV[j], g.dV[64 * j:64 * j + dV[j].shape[0]], rtol=0, atol=1e-12)
+    assert np.allclose(dW, g.dW, rtol=0, atol=1e-10)
