@@ -9,18 +9,23 @@
 //  k_mask_t    transposed block mask (row j = the query blocks that keep key
 //              block j), row-major and word-major, 64 x 64 bit tiles by wave
 //              ballots.
-//  k_bwd_q     one workgroup per query block.  D = rowsum(dO O_sparse) from
-//              the sparse output the forward kept; the linear branch (bf16
-//              MFMA on LDS tiles): phi(Q), O_l = phi(Q) H_i / den, G = dO W,
-//              d phi(Q) and its channel-softmax gradient, dH_i = phi(Q)^T G /
-//              den, dz_i.  Then the sparse dQ
-//              over the kept key blocks with one query per lane column
-//              (S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T);
-//              dQ is written once.
+//  k_bwd_qlin  one workgroup per query block, linear branch (bf16 MFMA on LDS
+//              tiles): phi(Q), O_l = phi(Q) H_i / den, G = dO W, d phi(Q) and
+//              its channel-softmax gradient (float32 rows), dH_i = phi(Q)^T G /
+//              den and dz_i (bf16), O_l rows (bf16, for dW).
+//  k_bwd_q     one workgroup per query block: D = rowsum(dO O_sparse) from
+//              the sparse output the forward kept, then the sparse dQ over the
+//              kept key blocks with one query per lane column (S^T = K Q^T,
+//              P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T); dQ (plus the
+//              linear part) is rounded once.
 //  k_marginal  (the forward's kernel) dHb = (1 - M)^T dH with the transposed mask.
+//  k_bwd_kvlin one workgroup per key block: the key side of the linear branch
+//              from dHb_j (float32 rows).
 //  k_bwd_kv    one workgroup per key block: dV^T += dO^T P and dK^T += Q^T dS
 //              over the query blocks that keep it (one key per lane column),
-//              then the key side of the linear branch from dHb_j; written once.
+//              plus the linear parts; rounded once.
+// The two sparse kernels fit two workgroups per CU (registers and LDS), so
+// one workgroup's tile loads overlap the other's products.
 //  k_bwd_dw    dW partials dO^T O_l per chunk of query blocks; k_dw_sum adds them.
 //
 // Precision: bf16 operands, float32 accumulation; P and dS are rounded to
@@ -144,55 +149,27 @@ __global__ __launch_bounds__(256) void k_mask_t(const uint64_t *__restrict__ mas
 // ---------------------------------------------------------------------------
 // dQ (and the linear branch's per-query-block gradients)
 // ---------------------------------------------------------------------------
-template <int D, bool LIN>
-__global__ __launch_bounds__(256) void k_bwd_q(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ W, const uint16_t *__restrict__ Os, const uint16_t *__restrict__ dO,
-    const uint16_t *__restrict__ hi, const float *__restrict__ lse, const int32_t *__restrict__ kept,
-    const float *__restrict__ mu, int N, int T, int kb, int F, float qk_scale, float sm_scale,
-    float *__restrict__ delta,
-    uint16_t *__restrict__ ol, uint16_t *__restrict__ dhi, uint16_t *__restrict__ dq) {
+// ---------------------------------------------------------------------------
+// Linear branch, query side: one workgroup per query block
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_qlin(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ W, const uint16_t *__restrict__ dO,
+    const uint16_t *__restrict__ hi, int N, int T, int F, uint16_t *__restrict__ ol,
+    uint16_t *__restrict__ dhi, float *__restrict__ dql_out) {
   using G = BTile<D>;
   constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
-  // region A: phi(Q), dO, O_l, dnum tiles (linear part), then the K and V
-  // double buffers; region B: W and H^T tiles, then dQ_linear in float32
+  // phi(Q), dO, O_l, dnum tiles; W and H^T tiles
   __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t rb[LIN ? 2 * D * P : 8];
-  __shared__ float sden[64], sdden[64], sdelta[64], sz[D];
+  __shared__ __attribute__((aligned(16))) uint16_t rb[2 * D * P];
+  __shared__ float sden[64], sdden[64], sz[D];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int qb = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = qb / T, i = qb - bh * T;
   const int ni = min(BLK, N - i * BLK);
   const size_t rowbase = (size_t)bh * N + (size_t)i * BLK;
   const uint16_t *Qb = Q + rowbase * D, *dOb = dO + rowbase * D;
-  const uint16_t *Osb = Os + (size_t)qb * BLK * D;  // O_sparse rows of this block
-  float *sql = (float *)rb;  // dQ_linear [64][D] after the linear part
-
-  {  // D = rowsum(dO O_sparse), four threads per row
-    constexpr int CPT = D / 4;
-    const int r = tid >> 2, part = tid & 3;
-    float s = 0.f;
-    if (r < ni) {
-#pragma unroll
-      for (int c = 0; c < CPT; c += 8) {
-        const uint4 a = *(const uint4 *)(dOb + (size_t)r * D + part * CPT + c);
-        const uint4 b = *(const uint4 *)(Osb + (size_t)r * D + part * CPT + c);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s = __builtin_fmaf(bf2f((uint16_t)(av[e >> 1] >> (16 * (e & 1)))),
-                             bf2f((uint16_t)(bv[e >> 1] >> (16 * (e & 1)))), s);
-      }
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if (part == 0) {
-      sdelta[r] = s;
-      delta[(size_t)qb * BLK + r] = s;
-    }
-  }
-
-  if constexpr (LIN) {
+  {
     uint16_t *sa = ra, *sdo = ra + TILE, *sol = ra + 2 * TILE, *sdn = ra + 3 * TILE;
     uint16_t *sw = rb, *sht = rb + D * P;
     const uint16_t *hp = hi + (size_t)qb * F;
@@ -337,12 +314,58 @@ __global__ __launch_bounds__(256) void k_bwd_q(
       const int row = x / (D / 8), c8 = (x - row * (D / 8)) * 8;
       *(uint4 *)(olb + (size_t)row * D + c8) = *(const uint4 *)(sol + row * P + c8);
     }
-    __syncthreads();  // region A and B free
+    float *dqb = dql_out + (size_t)qb * BLK * D;
 #pragma unroll
     for (int x = 0; x < CG; ++x)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sql[(16 * w + 4 * g + r) * D + 16 * x + l16] = dql[x][r];
+      for (int r = 0; r < 4; ++r) dqb[(size_t)(16 * w + 4 * g + r) * D + 16 * x + l16] = dql[x][r];
+    }
+}
+
+template <int D, bool LIN>
+__global__ __launch_bounds__(256, 2) void k_bwd_q(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ Os, const uint16_t *__restrict__ dO,
+    const float *__restrict__ lse, const int32_t *__restrict__ kept, const float *__restrict__ mu,
+    const float *__restrict__ dql, int N, int T, int kb, float qk_scale, float sm_scale,
+    float *__restrict__ delta, uint16_t *__restrict__ dq) {
+  using G = BTile<D>;
+  constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
+  // K and V double buffers
+  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
+  __shared__ float sdelta[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int qb = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = qb / T, i = qb - bh * T;
+  const int ni = min(BLK, N - i * BLK);
+  const size_t rowbase = (size_t)bh * N + (size_t)i * BLK;
+  const uint16_t *Qb = Q + rowbase * D, *dOb = dO + rowbase * D;
+  const uint16_t *Osb = Os + (size_t)qb * BLK * D;  // O_sparse rows of this block
+
+  {  // D = rowsum(dO O_sparse), four threads per row
+    constexpr int CPT = D / 4;
+    const int r = tid >> 2, part = tid & 3;
+    float s = 0.f;
+    if (r < ni) {
+#pragma unroll
+      for (int c = 0; c < CPT; c += 8) {
+        const uint4 a = *(const uint4 *)(dOb + (size_t)r * D + part * CPT + c);
+        const uint4 b = *(const uint4 *)(Osb + (size_t)r * D + part * CPT + c);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s = __builtin_fmaf(bf2f((uint16_t)(av[e >> 1] >> (16 * (e & 1)))),
+                             bf2f((uint16_t)(bv[e >> 1] >> (16 * (e & 1)))), s);
+      }
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) {
+      sdelta[r] = s;
+      delta[(size_t)qb * BLK + r] = s;
+    }
   }
+
   __syncthreads();
 
   // sparse dQ: wave w, lane column = query 16w + l16.  Since sum_s dS_rs = 0,
@@ -449,7 +472,7 @@ __global__ __launch_bounds__(256) void k_bwd_q(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v[r] = sm_scale * __builtin_fmaf(-dsrow, muh[16 * x + 4 * g + r], adq[x][r]);
-        if (LIN) v[r] += sql[q * D + 16 * x + 4 * g + r];
+        if (LIN) v[r] += dql[((size_t)qb * BLK + q) * D + 16 * x + 4 * g + r];
       }
       *(uint2 *)(dqr + 16 * x + 4 * g) = make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
     }
@@ -459,17 +482,99 @@ __global__ __launch_bounds__(256) void k_bwd_q(
 // ---------------------------------------------------------------------------
 // dK, dV (and the key side of the linear branch)
 // ---------------------------------------------------------------------------
-template <int D, bool LIN>
-__global__ __launch_bounds__(256) void k_bwd_kv(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
-    const uint64_t *__restrict__ mt, const uint16_t *__restrict__ dhb, int N, int T, int W64, int F,
-    float qk_scale, float sm_scale, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+// ---------------------------------------------------------------------------
+// Linear branch, key side: one workgroup per key block.  Hb_j = phi(K_j)^T V_j,
+// zb_j = phi(K_j)^T 1, so dV_lin = phi(K) dHb, d phi(K) = V dHb^T + dzb and
+// dK_lin = phi(K) (d phi - rowsum(phi d phi)); float32 rows for k_bwd_kv.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_kvlin(const uint16_t *__restrict__ K,
+                                                   const uint16_t *__restrict__ V,
+                                                   const uint16_t *__restrict__ dhb, int N, int T,
+                                                   int F, float *__restrict__ dkl,
+                                                   float *__restrict__ dvl) {
   using G = BTile<D>;
   constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
-  // Q and dO double buffers; afterwards phi(K), V and dHb^T tiles
   __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
-  __shared__ float sl[2][64], sd[2][64], szb[D];
+  __shared__ float szb[D];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int kblk = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = kblk / T, j = kblk - bh * T;
+  const int nj = min(BLK, N - j * BLK);
+  const size_t rowbase = (size_t)bh * N + (size_t)j * BLK;
+  const int s = 16 * w + l16;  // this lane column's key
+  v4f adv[CG];
+#pragma unroll
+  for (int x = 0; x < CG; ++x) adv[x] = v4f{0.f, 0.f, 0.f, 0.f};
+  {
+    // Hb_j = phi(K_j)^T V_j, zb_j = phi(K_j)^T 1: dV += phi(K) dHb,
+    // d phi(K) = V dHb^T + dzb, dK += phi(K) (d phi - rowsum(phi d phi))
+    uint16_t *sb = ra, *sv = ra + TILE, *sdh = ra + 2 * TILE;  // sdh: dHb^T [c2][c]
+    {
+      uint4 r[NPT];
+      tile_load<D>(V + rowbase * D, nj, r, tid);
+      tile_store<D>(r, sv, tid);
+    }
+    phi_rows<D>(K + rowbase * D, nj, sb, nullptr, tid);
+    const uint16_t *dh = dhb + (size_t)kblk * F;
+    for (int x = tid; x < D * D / 4; x += 256) {  // pieces of four consecutive c
+      const int fr = x >> 6, ln = x & 63;
+      const int ct = fr / CG, xt = fr - ct * CG;
+      const int c2 = 16 * xt + (ln & 15), c = 16 * ct + 4 * (ln >> 4);
+      *(uint2 *)(sdh + c2 * P + c) = *(const uint2 *)(dh + (size_t)x * 4);
+    }
+    if (tid < D) szb[tid] = bf2f(dh[D * D + tid]);
+    __syncthreads();
+    v4f aph[CG];
+#pragma unroll
+    for (int x = 0; x < CG; ++x) aph[x] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC32; ++kc) {
+      const v4u bfr = lds_rows(sb, P, 16 * w, kc, lane);  // phi(K): key column, k = c
+      const v4u vfr = lds_rows(sv, P, 16 * w, kc, lane);  // V: key column, k = c2
+#pragma unroll
+      for (int x = 0; x < CG; ++x) {
+        adv[x] = mfma_bf16(lds_rows(sdh, P, 16 * x, kc, lane), bfr, adv[x]);
+        aph[x] = mfma_bf16(lds_frag(sdh, P, kc, 16 * x, lane), vfr, aph[x]);
+      }
+    }
+    float bv[CG][4], dot = 0.f;
+#pragma unroll
+    for (int x = 0; x < CG; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * x + 4 * g + r;
+        bv[x][r] = bf2f(sb[s * P + c]);
+        aph[x][r] += szb[c];
+        dot += bv[x][r] * aph[x][r];
+      }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    if (s < nj) {
+      float *kl = dkl + ((size_t)kblk * BLK + s) * D, *vl = dvl + ((size_t)kblk * BLK + s) * D;
+#pragma unroll
+      for (int x = 0; x < CG; ++x) {
+        *(float4 *)(kl + 16 * x + 4 * g) =
+            make_float4(bv[x][0] * (aph[x][0] - dot), bv[x][1] * (aph[x][1] - dot),
+                        bv[x][2] * (aph[x][2] - dot), bv[x][3] * (aph[x][3] - dot));
+        *(float4 *)(vl + 16 * x + 4 * g) = make_float4(adv[x][0], adv[x][1], adv[x][2], adv[x][3]);
+      }
+    }
+    }
+}
+
+template <int D, bool LIN>
+__global__ __launch_bounds__(256, 2) void k_bwd_kv(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
+    const uint64_t *__restrict__ mt, const float *__restrict__ dkl, const float *__restrict__ dvl,
+    int N, int T, int W64, float qk_scale, float sm_scale, uint16_t *__restrict__ dk,
+    uint16_t *__restrict__ dv) {
+  using G = BTile<D>;
+  constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
+  // Q and dO double buffers
+  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
+  __shared__ float sl[2][64], sd[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int kblk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = kblk / T, j = kblk - bh * T;
@@ -591,59 +696,21 @@ __global__ __launch_bounds__(256) void k_bwd_kv(
     buf ^= 1;
   }
 
+  // dK = sm_scale dK_sparse + dK_linear, dV = dV_sparse + dV_linear
   float ok4[CG][4];
 #pragma unroll
   for (int x = 0; x < CG; ++x)
 #pragma unroll
     for (int r = 0; r < 4; ++r) ok4[x][r] = sm_scale * adk[x][r];
-  if constexpr (LIN) {
-    // Hb_j = phi(K_j)^T V_j, zb_j = phi(K_j)^T 1: dV += phi(K) dHb,
-    // d phi(K) = V dHb^T + dzb, dK += phi(K) (d phi - rowsum(phi d phi))
-    uint16_t *sb = ra, *sv = ra + TILE, *sdh = ra + 2 * TILE;  // sdh: dHb^T [c2][c]
-    {
-      uint4 r[NPT];
-      tile_load<D>(V + rowbase * D, nj, r, tid);
-      tile_store<D>(r, sv, tid);
+  if (LIN && s < nj) {
+    const float *kl = dkl + ((size_t)kblk * BLK + s) * D, *vl = dvl + ((size_t)kblk * BLK + s) * D;
+#pragma unroll
+    for (int x = 0; x < CG; ++x) {
+      const float4 a = *(const float4 *)(kl + 16 * x + 4 * g);
+      const float4 c = *(const float4 *)(vl + 16 * x + 4 * g);
+      ok4[x][0] += a.x; ok4[x][1] += a.y; ok4[x][2] += a.z; ok4[x][3] += a.w;
+      adv[x][0] += c.x; adv[x][1] += c.y; adv[x][2] += c.z; adv[x][3] += c.w;
     }
-    phi_rows<D>(K + rowbase * D, nj, sb, nullptr, tid);
-    const uint16_t *dh = dhb + (size_t)kblk * F;
-    for (int x = tid; x < D * D / 4; x += 256) {  // pieces of four consecutive c
-      const int fr = x >> 6, ln = x & 63;
-      const int ct = fr / CG, xt = fr - ct * CG;
-      const int c2 = 16 * xt + (ln & 15), c = 16 * ct + 4 * (ln >> 4);
-      *(uint2 *)(sdh + c2 * P + c) = *(const uint2 *)(dh + (size_t)x * 4);
-    }
-    if (tid < D) szb[tid] = bf2f(dh[D * D + tid]);
-    __syncthreads();
-    v4f aph[CG];
-#pragma unroll
-    for (int x = 0; x < CG; ++x) aph[x] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < KC32; ++kc) {
-      const v4u bfr = lds_rows(sb, P, 16 * w, kc, lane);  // phi(K): key column, k = c
-      const v4u vfr = lds_rows(sv, P, 16 * w, kc, lane);  // V: key column, k = c2
-#pragma unroll
-      for (int x = 0; x < CG; ++x) {
-        adv[x] = mfma_bf16(lds_rows(sdh, P, 16 * x, kc, lane), bfr, adv[x]);
-        aph[x] = mfma_bf16(lds_frag(sdh, P, kc, 16 * x, lane), vfr, aph[x]);
-      }
-    }
-    float bv[CG][4], dot = 0.f;
-#pragma unroll
-    for (int x = 0; x < CG; ++x)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * x + 4 * g + r;
-        bv[x][r] = bf2f(sb[s * P + c]);
-        aph[x][r] += szb[c];
-        dot += bv[x][r] * aph[x][r];
-      }
-    dot += __shfl_xor(dot, 16, 64);
-    dot += __shfl_xor(dot, 32, 64);
-#pragma unroll
-    for (int x = 0; x < CG; ++x)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ok4[x][r] += bv[x][r] * (aph[x][r] - dot);
   }
   if (s < nj) {
     uint16_t *dkr = dk + (rowbase + s) * D, *dvr = dv + (rowbase + s) * D;
@@ -724,17 +791,22 @@ __global__ void k_fill_zero_f32(float *__restrict__ x, int n) {
 
 template <int D, bool LIN>
 static void launch_bwd_t(const Plan &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const uint16_t *w, const uint16_t *dout,
-                         uint16_t *dq, uint16_t *dk, uint16_t *dv, const WsPtrs &ws,
-                         hipStream_t st) {
+                         const uint16_t *w, const uint16_t *dout, uint16_t *dq, uint16_t *dk,
+                         uint16_t *dv, const WsPtrs &ws, hipStream_t st) {
   const float qk_scale = p.sm_scale * BWD_LOG2E;
   const int nqb = p.BH * p.T;
-  hipLaunchKernelGGL((k_bwd_q<D, LIN>), dim3(nqb), dim3(256), 0, st, q, k, v, w, ws.os, dout, ws.hi,
-                     ws.lse, ws.kept, ws.mu, p.N, p.T, p.kb, p.F, qk_scale, p.sm_scale, ws.delta, ws.ol,
-                     ws.dhi, dq);
-  if (LIN) launch_marginal_ptrs(p, ws.mtt, ws.dhi, ws.dhb, st);
+  if (LIN)
+    hipLaunchKernelGGL(k_bwd_qlin<D>, dim3(nqb), dim3(256), 0, st, q, w, dout, ws.hi, p.N, p.T,
+                       p.F, ws.ol, ws.dhi, ws.dql);
+  hipLaunchKernelGGL((k_bwd_q<D, LIN>), dim3(nqb), dim3(256), 0, st, q, k, v, ws.os, dout, ws.lse,
+                     ws.kept, ws.mu, ws.dql, p.N, p.T, p.kb, qk_scale, p.sm_scale, ws.delta, dq);
+  if (LIN) {
+    launch_marginal_ptrs(p, ws.mtt, ws.dhi, ws.dhb, st);
+    hipLaunchKernelGGL(k_bwd_kvlin<D>, dim3(nqb), dim3(256), 0, st, k, v, ws.dhb, p.N, p.T, p.F,
+                       ws.dkl, ws.dvl);
+  }
   hipLaunchKernelGGL((k_bwd_kv<D, LIN>), dim3(nqb), dim3(256), 0, st, q, k, v, dout, ws.lse,
-                     ws.delta, ws.mt, ws.dhb, p.N, p.T, p.W64, p.F, qk_scale, p.sm_scale, dk, dv);
+                     ws.delta, ws.mt, ws.dkl, ws.dvl, p.N, p.T, p.W64, qk_scale, p.sm_scale, dk, dv);
 }
 
 void launch_bwd(const Plan &p, const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -47,6 +47,9 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.dhb = (uint16_t *)(b + p.off[R_DHB]);
   w.dwp = (float *)(b + p.off[R_DWP]);
   w.os = p.size[R_OS] ? (uint16_t *)(b + p.off[R_OS]) : nullptr;
+  w.dql = (float *)(b + p.off[R_DQL]);
+  w.dkl = (float *)(b + p.off[R_DKL]);
+  w.dvl = (float *)(b + p.off[R_DVL]);
   return w;
 }
 
@@ -158,6 +161,9 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_DHI] = p.bwd && p.lin_on ? bt * p.F * 2 : 0;
   p.size[R_DHB] = p.bwd && p.lin_on ? bt * p.F * 2 : 0;
   p.size[R_DWP] = p.bwd && p.lin_on ? (size_t)p.dw_chunks * p.d * p.d * 4 : 0;
+  p.size[R_DQL] = p.bwd && p.lin_on ? blk_elems * 4 : 0;
+  p.size[R_DKL] = p.bwd && p.lin_on ? blk_elems * 4 : 0;
+  p.size[R_DVL] = p.bwd && p.lin_on ? blk_elems * 4 : 0;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
     p.off[r] = o;

@@ -41,6 +41,9 @@ enum Region {
   R_DHI,  // bf16 gradient of the marginal state (dh_off order)  [BH][T][F]
   R_DHB,  // bf16 gradient of the key-block state (same order)   [BH][T][F]
   R_DWP,  // f32 partial projection gradients                    [nchunk][d][d]
+  R_DQL,  // f32 linear-branch dQ rows                           [BH][T][64][d]
+  R_DKL,  // f32 linear-branch dK rows                           [BH][T][64][d]
+  R_DVL,  // f32 linear-branch dV rows                           [BH][T][64][d]
   R_COUNT
 };
 
@@ -59,7 +62,7 @@ struct Plan {
 };
 
 struct WsPtrs {
-  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn, *dkx, *lse, *delta, *dwp;
+  float *qbar, *ksum, *kbar, *mu, *dq, *dk, *dkn, *dkx, *lse, *delta, *dwp, *dql, *dkl, *dvl;
   uint64_t *mt, *mtt;
   uint16_t *ol, *dhi, *dhb, *os;
   uint64_t *mask, *maskt;
