@@ -75,6 +75,54 @@ __device__ __forceinline__ void tile_store(const uint4 (&r)[BTile<D>::NPT], uint
   }
 }
 
+// Tiles of the two sparse loops: 64 rows of D bf16 without padding, the
+// 4-element (8-byte) units of row r XOR-swizzled by sw_unit(r).  The row
+// reads of an MFMA operand (16 consecutive rows at one unit) and the
+// transposing reads (4 consecutive rows at 4 consecutive units) then fall on
+// distinct banks; with a padded pitch one of the two patterns always
+// conflicts.
+__device__ __forceinline__ int sw_unit(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// element offset of (r, c) for c % 4 == 0
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int c) {
+  return r * D + ((((c >> 2) ^ sw_unit(r))) << 2);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store_sw(const uint4 (&r)[BTile<D>::NPT], uint16_t *lds,
+                                              int tid) {
+#pragma unroll
+  for (int e = 0; e < BTile<D>::NPT; ++e) {
+    const int x = tid + 256 * e;
+    const int row = x / (D / 8), c8 = (x - row * (D / 8)) * 8;
+    *(uint2 *)(lds + sw_off<D>(row, c8)) = make_uint2(r[e].x, r[e].y);
+    *(uint2 *)(lds + sw_off<D>(row, c8 + 4)) = make_uint2(r[e].z, r[e].w);
+  }
+}
+
+// lds_rows on a swizzled tile
+template <int D>
+__device__ __forceinline__ v4u sw_rows(const uint16_t *tile, int r0, int kc, int lane) {
+  const int r = r0 + (lane & 15), k0 = 32 * kc + 4 * (lane >> 4);
+  const uint2 lo = *(const uint2 *)(tile + sw_off<D>(r, k0));
+  const uint2 hi = *(const uint2 *)(tile + sw_off<D>(r, k0 + 16));
+  return v4u{lo.x, lo.y, hi.x, hi.y};
+}
+
+// lds_frag on a swizzled tile: rows 32 kc2 + 4g + 0..3 and 32 kc2 + 16 + 4g
+// + 0..3 of column n0 + l%16, through the transposing read
+template <int D>
+__device__ __forceinline__ v4u sw_frag(const uint16_t *tile, int kc2, int n0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int rlo = 32 * kc2 + 4 * g + (j >> 2), c = n0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
+  const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16 *)(tile + sw_off<D>(rlo, c)));
+  const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16 *)(tile + sw_off<D>(rlo + 16, c)));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return v4u{a.x, a.y, b.x, b.y};
+}
+
 // phi of 64 rows (softmax over the D channels, rounded to bf16) into an LDS
 // tile, four threads per row; rows >= nvalid become 0.  Returns this
 // thread's partial dot of its phi values with zg (global bf16 [D]) when
@@ -331,8 +379,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
     float *__restrict__ delta, uint16_t *__restrict__ dq) {
   using G = BTile<D>;
   constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
-  // K and V double buffers
-  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
+  // K and V double buffers (swizzled tiles of 64 D elements)
+  constexpr int ST = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * ST];
   __shared__ float sdelta[64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int qb = xcd_remap(blockIdx.x, gridDim.x);
@@ -404,8 +453,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
       const int j = kl[0];
       tile_load<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
       tile_load<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
-      tile_store<D>(rk, ra, tid);
-      tile_store<D>(rv, ra + TILE, tid);
+      tile_store_sw<D>(rk, ra, tid);
+      tile_store_sw<D>(rv, ra + ST, tid);
     }
     __syncthreads();
     for (int n = 0; n < kb; ++n) {
@@ -415,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
         tile_load<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
         tile_load<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
       }
-      const uint16_t *sk = ra + 2 * cur * TILE, *sv = sk + TILE;
+      const uint16_t *sk = ra + 2 * cur * ST, *sv = sk + ST;
       const int nj = min(BLK, N - kl[n] * BLK);  // padding keys get dS = 0
       v4f s[4], dp[4];
 #pragma unroll
@@ -424,8 +473,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
       for (int kc = 0; kc < KC32; ++kc)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          s[t] = mfma_bf16(lds_rows(sk, P, 16 * t, kc, lane), qf[kc], s[t]);
-          dp[t] = mfma_bf16(lds_rows(sv, P, 16 * t, kc, lane), of[kc], dp[t]);
+          s[t] = mfma_bf16(sw_rows<D>(sk, 16 * t, kc, lane), qf[kc], s[t]);
+          dp[t] = mfma_bf16(sw_rows<D>(sv, 16 * t, kc, lane), of[kc], dp[t]);
         }
       // dS^T = P^T (dP^T - D) in the key order of lds_frag (kmaj)
       v4u dsb[2];
@@ -451,10 +500,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
-        for (int x = 0; x < CG; ++x) adq[x] = mfma_bf16(lds_frag(sk, P, kc2, 16 * x, lane), dsb[kc2], adq[x]);
+        for (int x = 0; x < CG; ++x) adq[x] = mfma_bf16(sw_frag<D>(sk, kc2, 16 * x, lane), dsb[kc2], adq[x]);
       if (n + 1 < kb) {
-        tile_store<D>(rk, ra + 2 * (cur ^ 1) * TILE, tid);
-        tile_store<D>(rv, ra + (2 * (cur ^ 1) + 1) * TILE, tid);
+        tile_store_sw<D>(rk, ra + 2 * (cur ^ 1) * ST, tid);
+        tile_store_sw<D>(rv, ra + (2 * (cur ^ 1) + 1) * ST, tid);
       }
       __syncthreads();
     }
@@ -572,8 +621,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     uint16_t *__restrict__ dv) {
   using G = BTile<D>;
   constexpr int P = G::P, CG = G::CG, KC32 = G::KC32, TILE = G::TILE, NPT = G::NPT;
-  // Q and dO double buffers
-  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * TILE];
+  // Q and dO double buffers (swizzled tiles of 64 D elements)
+  constexpr int ST = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t ra[4 * ST];
   __shared__ float sl[2][64], sd[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int kblk = xcd_remap(blockIdx.x, gridDim.x);
@@ -630,8 +680,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     }
   };
   auto store_block = [&](int b) {
-    tile_store<D>(rq, ra + 2 * b * TILE, tid);
-    tile_store<D>(ro, ra + (2 * b + 1) * TILE, tid);
+    tile_store_sw<D>(rq, ra + 2 * b * ST, tid);
+    tile_store_sw<D>(ro, ra + (2 * b + 1) * ST, tid);
     if (tid < BLK) {
       sl[b][tid] = lsn;
       sd[b][tid] = dn;
@@ -647,7 +697,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
   while (inext >= 0) {
     inext = next_i();
     if (inext >= 0) load_block(inext);
-    const uint16_t *sq = ra + 2 * buf * TILE, *so = sq + TILE;
+    const uint16_t *sq = ra + 2 * buf * ST, *so = sq + ST;
     // S and dP: query rows 16t + 4g + r, key column s
     v4f sa[4], dp[4];
 #pragma unroll
@@ -656,8 +706,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     for (int kc = 0; kc < KC32; ++kc)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        sa[t] = mfma_bf16(lds_rows(sq, P, 16 * t, kc, lane), kf[kc], sa[t]);
-        dp[t] = mfma_bf16(lds_rows(so, P, 16 * t, kc, lane), vf[kc], dp[t]);
+        sa[t] = mfma_bf16(sw_rows<D>(sq, 16 * t, kc, lane), kf[kc], sa[t]);
+        dp[t] = mfma_bf16(sw_rows<D>(so, 16 * t, kc, lane), vf[kc], dp[t]);
       }
     // P and dS as B fragments in the query order of lds_frag
     v4u pb[2], dsb[2];
@@ -688,8 +738,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
       for (int x = 0; x < CG; ++x) {
-        adv[x] = mfma_bf16(lds_frag(so, P, kc2, 16 * x, lane), pb[kc2], adv[x]);
-        adk[x] = mfma_bf16(lds_frag(sq, P, kc2, 16 * x, lane), dsb[kc2], adk[x]);
+        adv[x] = mfma_bf16(sw_frag<D>(so, kc2, 16 * x, lane), pb[kc2], adv[x]);
+        adk[x] = mfma_bf16(sw_frag<D>(sq, kc2, 16 * x, lane), dsb[kc2], adk[x]);
       }
     if (inext >= 0) store_block(buf ^ 1);
     __syncthreads();
