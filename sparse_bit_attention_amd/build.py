@@ -35,9 +35,7 @@ FLAGS = [
 ]
 
 
-# Per-file extra flags.  The attention kernel keeps its MFMA results in VGPRs:
-# its softmax reads the QK^T accumulators with vector ALU code, and the AGPR
-# form would add an AGPR -> VGPR copy per score.
+# Per-file extra hipcc flags (none at present; e.g. {"k_attn.hip": [...]}).
 EXTRA = {}
 
 
