@@ -1,0 +1,69 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard and the work
+counts behind its roofline figures."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from sparse_bit_attention_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+@pytest.mark.parametrize("n", ["2", "8"])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_attention_work_at_720p():
+    """Kept pairs and MFMA work of the Wan-14B-720P layer: 40 heads x 1182
+    query blocks x 118 kept blocks; per pair 2*64*64*128 ops for QK^T and as
+    many bf16 flops for PV; per query block 4*64*d^2 for the linear epilogue."""
+    b = load_bench()
+    wl = synth.WORKLOADS["wan14b-720p"]
+    i8, bf, pairs = b.attn_work(wl, 118, 1182)
+    assert pairs == 40 * 1182 * 118 == 5_579_040
+    assert i8 == pairs * 2 * 64 * 64 * 128
+    assert bf == pairs * 2 * 64 * 64 * 128 + 40 * 1182 * 4 * 64 * 128 * 128
+    z, bf2, _ = b.attn_work(wl, 118, 1182, qk_int8=False)
+    assert z == 0 and bf2 == bf + i8
+    # no linear term when every block is kept
+    wl1 = synth.Workload("all", 1, 1, 640, 128, 1.0)
+    assert b.attn_work(wl1, 10, 10)[1] == 10 * 10 * 2 * 64 * 64 * 128
+
+
+def test_backward_work_at_720p():
+    b = load_bench()
+    wl = synth.WORKLOADS["wan14b-720p"]
+    pairs = 40 * 1182 * 118
+    F = (128 * 128 + 128 + 127) // 128 * 128
+    expect = (pairs * 7 * 2 * 64 * 64 * 128 + 40 * 1182 * 7 * 2 * 64 * 128 * 128
+              + 40 * 2.0 * 1182 * 1182 * F)
+    assert b.bwd_work(wl, 1182, 118) == pytest.approx(expect, rel=1e-12)
+
+
+def test_traffic_entry_is_null_or_positive():
+    """The HBM-traffic figure comes from the committed counter summary and is
+    reported only while that summary was taken on the current kernel source."""
+    b = load_bench()
+    t = b.traffic_entry()
+    assert t is None or t > 0
+    meta = json.load(open(b.TRAFFIC_FILE))
+    if meta.get("kernel_src_sha256_16") == b.src_hash(b.ATTN_SRC):
+        assert t == meta["bytes_per_launch"]
+    else:
+        assert t is None
