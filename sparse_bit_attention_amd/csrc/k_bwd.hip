@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void k_bwd_qlin(
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int x = 0; x < CG; ++x)
-        *(uint2 *)(dh + (((CT * w + ct) * CG + x) * 64 + lane) * 4) =
+        *(uint2 *)(dh + dh_off(16 * (CT * w + ct) + 4 * g, 16 * x + l16, CG)) =
             make_uint2(pack2bf(ah[ct][x][0], ah[ct][x][1]), pack2bf(ah[ct][x][2], ah[ct][x][3]));
     if (tid < D) {  // dz_i[c] = sum_r phi(Q)[r][c] dden[r]
       float s = 0.f;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
   for (int x = 0; x < CG; ++x) adq[x] = v4f{0.f, 0.f, 0.f, 0.f};
   float dsrow = 0.f;  // this lane's share of rowsum(dS) for query q
   if (kb > 0) {
-    // buffer b: K at ra + 2 b TILE, V at ra + (2 b + 1) TILE
+    // buffer b: K at ra + 2 b ST, V at ra + (2 b + 1) ST
     v4u qf[KC32], of[KC32];
 #pragma unroll
     for (int kc = 0; kc < KC32; ++kc) {
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     return 64 * wc + b;
   };
   const size_t headrow = (size_t)bh * N;
-  // buffer b: Q at ra + 2 b TILE, dO at ra + (2 b + 1) TILE
+  // buffer b: Q at ra + 2 b ST, dO at ra + (2 b + 1) ST
   uint4 rq[NPT], ro[NPT];
   float lsn = INFINITY, dn = 0.f;
   auto load_block = [&](int i) {
