@@ -290,16 +290,21 @@ struct QKOps {
   static __device__ __forceinline__ float nm(float c, float m) { return -__builtin_fmaf(ZERO, c, m); }
 };
 
-template <int D, bool QK8>
+#ifndef SLA_FINE_KLEAD
+#define SLA_FINE_KLEAD 3
+#define SLA_FINE_VLEAD 4
+#endif
+template <int D, bool QK8, bool FINE = false>
 struct Pipe {
   static constexpr int KC = QKOps<D, QK8>::NK, CG = D / 16;
   static constexpr int KT = KC;          // 1 KiB fragments per K tile (16 keys)
   static constexpr int VQ = CG / 2;      // 1 KiB fragments per V quarter
   // K tile sigma + KLEAD and V quarter sigma + VLEAD are loaded at sub-stage
   // sigma; bf16 Q and K fragments take twice the registers of INT8 ones, so
-  // that path keeps shorter rings
-  static constexpr int KLEAD = QK8 ? 4 : 2;
-  static constexpr int VLEAD = QK8 ? 4 : 2;
+  // that path keeps shorter rings, and so does the fine-scale path, whose
+  // per-lane key scales would otherwise spill
+  static constexpr int KLEAD = QK8 ? (FINE ? SLA_FINE_KLEAD : 4) : 2;
+  static constexpr int VLEAD = QK8 ? (FINE ? SLA_FINE_VLEAD : 4) : 2;
 };
 
 // Probabilities: p = exp2(score * c + nm) cut to bf16 by keeping the upper
@@ -341,7 +346,7 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
                                           const PipeBlocks &pb, const v4u (&lm)[2],
                                           const uint4 *kload_src, const uint4 *vload_src,
                                           int lane) {
-  using P = Pipe<D, QK8>;
+  using P = Pipe<D, QK8, FINE>;
   using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, VQ = P::VQ;
   // loads: K tile sigma+KLEAD, V quarter sigma+VLEAD, kept together at the
@@ -439,7 +444,7 @@ __device__ __forceinline__ void kept_loop_piped(
     const float (&m)[4], float (&lsum)[4], const int32_t *kl, int kb, const float *dk,
     const uint4 *k8u, const uint4 *vtu, size_t headblk, const float (&dqi)[4], int T, int nlast,
     int lane) {
-  using P = Pipe<D, QK8>;
+  using P = Pipe<D, QK8, FINE>;
   using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, CG = P::CG, VQ = P::VQ, KT = P::KT;
   constexpr int KFR = 4 * KT, VFR = 4 * VQ;  // fragments per block
