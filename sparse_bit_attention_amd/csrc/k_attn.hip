@@ -290,10 +290,6 @@ struct QKOps {
   static __device__ __forceinline__ float nm(float c, float m) { return -__builtin_fmaf(ZERO, c, m); }
 };
 
-#ifndef SLA_FINE_KLEAD
-#define SLA_FINE_KLEAD 3
-#define SLA_FINE_VLEAD 4
-#endif
 template <int D, bool QK8, bool FINE = false>
 struct Pipe {
   static constexpr int KC = QKOps<D, QK8>::NK, CG = D / 16;
@@ -301,10 +297,11 @@ struct Pipe {
   static constexpr int VQ = CG / 2;      // 1 KiB fragments per V quarter
   // K tile sigma + KLEAD and V quarter sigma + VLEAD are loaded at sub-stage
   // sigma; bf16 Q and K fragments take twice the registers of INT8 ones, so
-  // that path keeps shorter rings, and so does the fine-scale path, whose
-  // per-lane key scales would otherwise spill
-  static constexpr int KLEAD = QK8 ? (FINE ? SLA_FINE_KLEAD : 4) : 2;
-  static constexpr int VLEAD = QK8 ? (FINE ? SLA_FINE_VLEAD : 4) : 2;
+  // that path keeps shorter rings.  INT8: a K ring of 3 leaves the fine-scale
+  // path's per-lane key scales room in the register file (4 spills) and
+  // saves the block-scale path a few accumulator copies (1.6% faster than 4).
+  static constexpr int KLEAD = QK8 ? 3 : 2;
+  static constexpr int VLEAD = QK8 ? 4 : 2;
 };
 
 // Probabilities: p = exp2(score * c + nm) cut to bf16 by keeping the upper
