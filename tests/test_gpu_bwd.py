@@ -238,3 +238,17 @@ def test_backward_full_length_two_heads_dw():
     the whole projection gradient (a sum over every row of every head)."""
     wl = synth.Workload("wan14b-720p-h2", 1, 2, 21 * 45 * 80, 128, 0.1)
     sampled_compare(wl, wl.heads(), check_dw=True)
+
+
+def test_backward_plan_forward_is_unchanged():
+    """A backward plan's forward also stores the row normalisers and O_sparse;
+    its output is bit-identical to a forward-only plan's."""
+    wl = synth.Workload("bwd-fwd-same", 1, 2, 1500, 128, 0.2, seed=55)
+    q, k, v, w = synth.all_inputs(wl)
+    Q, K, V, W = dev(q), dev(k), dev(v), dev(w)
+    outs = []
+    for backward in (False, True):
+        m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, qk_int8=False, backward=backward)
+        outs.append(m(Q, K, V, W))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
