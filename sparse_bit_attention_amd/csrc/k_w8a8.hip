@@ -99,8 +99,9 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
                                                       const int8_t *__restrict__ wq,
                                                       const float *__restrict__ sw, int M, int N,
                                                       int K, uint16_t *__restrict__ y) {
-  // two stages of [A 128 rows | B 256 rows] x 144 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(GM_BM + GM_BN) * GM_PITCH];
+  // two stages of [A 128 rows | B 256 rows] x 128 bytes
+  constexpr int STG = (GM_BM + GM_BN) * GM_PITCH;  // bytes per stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STG];
   // Tile order: groups of GM_G row tiles; inside a group the row tile runs
   // fastest, so consecutive workgroups (one XCD, xcd_remap) share a W tile
   // and a group's X tiles are reused across all column tiles.
@@ -119,25 +120,44 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
   const int nb = min((n0 + 64 * wc) / WB, (N - 1) / WB);
 
   // global -> LDS staging: 384 rows x 8 pieces of 16 bytes, 6 per thread;
-  // piece q = it * 512 + tid: row q / 8 (A rows first), piece q % 8.  Rows
-  // past M / N read the last row (never stored).
-  uint4 stg[6];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int it = 0; it < 6; ++it) {
-      const int q = it * 512 + tid, row = q >> 3, pc = q & 7;
-      const int8_t *src = row < GM_BM ? xq + (size_t)min(m0 + row, M - 1) * K
-                                      : wq + (size_t)min(n0 + row - GM_BM, N - 1) * K;
-      stg[it] = *(const uint4 *)(src + (size_t)kb * GM_BK + 16 * pc);
-    }
-  };
-  auto lstore = [&](int s) {
-#pragma unroll
-    for (int it = 0; it < 6; ++it) {
-      const int q = it * 512 + tid, row = q >> 3, pc = q & 7;
-      *(uint4 *)(&lds[s][row * GM_PITCH + 16 * (pc ^ (row & 7))]) = stg[it];
-    }
-  };
+  // piece it = 0..5 of this thread is row (it * 512 + tid) / 8 (A rows
+  // first), 16-byte piece tid % 8.  Rows past M / N read the last row
+  // (their products are never stored).  The six pieces sit in named
+  // registers: an indexed array here is moved by the compiler into LDS (or
+  // scratch), which costs a second LDS round trip per piece.
+  const int pc = tid & 7;
+  const int8_t *sr0, *sr1, *sr2, *sr3, *sr4, *sr5;
+  int lo0, lo1, lo2, lo3, lo4, lo5;  // LDS byte offsets inside a stage
+#define W8_SRC(I)                                                                          \
+  {                                                                                        \
+    const int row = (I * 512 + tid) >> 3;                                                  \
+    sr##I = (row < GM_BM ? xq + (size_t)min(m0 + row, M - 1) * K                           \
+                         : wq + (size_t)min(n0 + row - GM_BM, N - 1) * K) + 16 * pc;       \
+    lo##I = row * GM_PITCH + 16 * (pc ^ (row & 7));                                        \
+  }
+  W8_SRC(0) W8_SRC(1) W8_SRC(2) W8_SRC(3) W8_SRC(4) W8_SRC(5)
+#undef W8_SRC
+  uint4 g0, g1, g2, g3, g4, g5;
+#define W8_GLOAD(kb_)                                          \
+  {                                                            \
+    const size_t ko = (size_t)(kb_) * GM_BK;                   \
+    g0 = *(const uint4 *)(sr0 + ko);                           \
+    g1 = *(const uint4 *)(sr1 + ko);                           \
+    g2 = *(const uint4 *)(sr2 + ko);                           \
+    g3 = *(const uint4 *)(sr3 + ko);                           \
+    g4 = *(const uint4 *)(sr4 + ko);                           \
+    g5 = *(const uint4 *)(sr5 + ko);                           \
+  }
+#define W8_LSTORE(s_)                                          \
+  {                                                            \
+    uint8_t *st_ = lds + (s_) * STG;                           \
+    *(uint4 *)(st_ + lo0) = g0;                                \
+    *(uint4 *)(st_ + lo1) = g1;                                \
+    *(uint4 *)(st_ + lo2) = g2;                                \
+    *(uint4 *)(st_ + lo3) = g3;                                \
+    *(uint4 *)(st_ + lo4) = g4;                                \
+    *(uint4 *)(st_ + lo5) = g5;                                \
+  }
 
   v4f acc[4][4];
 #pragma unroll
@@ -145,22 +165,22 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
+  W8_GLOAD(0)
+  W8_LSTORE(0)
   __syncthreads();
   for (int kb = 0; kb < KB; ++kb) {
     const int s = kb & 1;
-    if (kb + 1 < KB) gload(kb + 1);
+    if (kb + 1 < KB) W8_GLOAD(kb + 1)
     // exact int32 block products: lane (row 16 i + l%16, group g) reads
     // bytes 64 kc + 16 g .. +15 of its row
     v4i af[4][2], bf[4][2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i][kc] = *(const v4i *)(&lds[s][lds_off(64 * wr + 16 * i, kc, lane)]);
+      for (int i = 0; i < 4; ++i) af[i][kc] = *(const v4i *)(lds + s * STG + lds_off(64 * wr + 16 * i, kc, lane));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j][kc] = *(const v4i *)(&lds[s][lds_off(GM_BM + 64 * wc + 16 * j, kc, lane)]);
+        bf[j][kc] = *(const v4i *)(lds + s * STG + lds_off(GM_BM + 64 * wc + 16 * j, kc, lane));
     }
     // Tile t = (i, j): its two MFMAs (the exact int32 block product), then
     // the fold of tile t-1 into the float32 sums, one fma by sx * sw per
@@ -183,9 +203,11 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kb + 1 < KB) lstore(s ^ 1);
+    if (kb + 1 < KB) W8_LSTORE(s ^ 1)
     __syncthreads();
   }
+#undef W8_GLOAD
+#undef W8_LSTORE
   // store bf16: lane holds rows 4 (l/16) + r of column l%16 of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
