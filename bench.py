@@ -8,9 +8,12 @@
 One step = the whole forward (sla_quantize, then sla_prepare_kv and
 sla_attend) over one batch of seeded synthetic inputs already resident in
 HBM.  Prints one JSON line: dense-equivalent TFLOP/s (4*B*H*N^2*d per call /
-time), ms per call, the per-stage times, the roofline of the dominant kernel
-(the block-sparse attention kernel, timed with HIP events on the stream it
-runs on) and the CPU oracle timed on a bounded sample of the same workload.
+time), ms per call (mean, and p10 / median / p90 of the per-call times), the
+per-stage times, the roofline of the dominant kernel (the block-sparse
+attention kernel, timed with HIP events on the stream it runs on) against the
+published peaks and against peaks measured on the same GPU after the timed
+region (MFMA-only kernels, a device copy), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,6 +77,27 @@ def traffic_entry():
     if t.get("kernel_src_sha256_16") != src_hash(ATTN_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+def measured_peaks():
+    """The GPU's own ceilings, measured after the timed region: MFMA-only
+    kernels per operand type (best of the 16x16 and 32x32 forms) and a plain
+    device copy.  Returned in the units the JSON line uses."""
+    from sparse_bit_attention_amd import peak
+    r = peak.measure()
+    return {
+        "int8_TOPs": r["int8"] / 1e12,
+        "bf16_TFLOPs": r["bf16"] / 1e12,
+        "hbm_copy_GBs": r["hbm_copy"] / 1e9,
+        "per_instruction_T": {k: v / 1e12 for k, v in r["mfma"].items()},
+        "how": "MFMA-only kernels, 8 waves per SIMD, independent accumulator chains, best of 3 "
+               "launches of ~25 ms; copy = torch device copy of 1 GiB (read + write bytes)",
+    }
+
+
+def spread(ms):
+    """p10, median and p90 of per-call times (ms)."""
+    return [float(np.percentile(ms, 10)), float(np.median(ms)), float(np.percentile(ms, 90))]
 
 
 def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True, fine=False):
@@ -158,6 +182,7 @@ def bench_w8a8(args, dev):
     g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     ops = 2.0 * lw.M * lw.N * lw.K
     log(f"[bench] ms/step {ms_step:.3f} (quantize X {q_ms:.3f}, gemm {g_ms:.3f})")
+    mp = measured_peaks()
     res = {
         "metric": "W8A8 block-128 linear layer TOPS (INT8 MFMA), Wan-14B-720P projection shape",
         "value": ops / (ms_step * 1e-3) / 1e12,
@@ -167,9 +192,13 @@ def bench_w8a8(args, dev):
         "data": "synthetic",
         "config": {"workload": lw.name, "M": lw.M, "N": lw.N, "K": lw.K, "block": 128},
         "stage_ms": {"sla_quant_b128(X)": q_ms, "sla_w8a8_gemm": g_ms},
+        "ms_per_call_p10_median_p90": spread([e[0].elapsed_time(e[2]) for e in events]),
         "roofline": {"kernel": "k_w8a8_gemm", "bound": "mfma", "achieved": ops / (g_ms * 1e-3) / 1e12,
                      "peak": P_I8 / 1e12, "unit": "TOP/s",
-                     "frac": ops / (g_ms * 1e-3) / P_I8, "traffic": None},
+                     "frac": ops / (g_ms * 1e-3) / P_I8, "traffic": None,
+                     "peak_measured": mp["int8_TOPs"],
+                     "frac_of_measured": ops / (g_ms * 1e-3) / 1e12 / mp["int8_TOPs"]},
+        "measured_peaks": mp,
     }
     if args.cpu_blocks > 0:
         # the oracle on a sample: rows of one 128-row block against all N columns
@@ -258,6 +287,7 @@ def bench_bwd(args, dev):
     log(f"[bench] ms/step {ms_step:.3f} (forward {f_ms:.3f}, backward {b_ms:.3f})")
     dense = 10.0 * wl.B * wl.H * wl.N * wl.N * wl.d
     flops = bwd_work(wl, T, kb)
+    mp = measured_peaks()
     res = {
         "metric": "SLA backward (bf16 QK^T, block mask fixed), dense-equivalent TFLOP/s",
         "value": dense / (b_ms * 1e-3) / 1e12,
@@ -268,9 +298,13 @@ def bench_bwd(args, dev):
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "block": 64,
                    "topk": wl.topk, "kb": kb, "use_linear": wl.use_linear},
         "stage_ms": {"forward (sla_quantize + sla_attention_fwd)": f_ms, "sla_attention_bwd": b_ms},
+        "bwd_ms_p10_median_p90": spread([e[1].elapsed_time(e[2]) for e in events]),
         "roofline": {"kernel": "sla_attention_bwd (all backward kernels)", "bound": "mfma",
                      "achieved": flops / (b_ms * 1e-3) / 1e12, "peak": P_BF16 / 1e12,
-                     "unit": "TFLOP/s", "frac": flops / (b_ms * 1e-3) / P_BF16, "traffic": None},
+                     "unit": "TFLOP/s", "frac": flops / (b_ms * 1e-3) / P_BF16, "traffic": None,
+                     "peak_measured": mp["bf16_TFLOPs"],
+                     "frac_of_measured": flops / (b_ms * 1e-3) / 1e12 / mp["bf16_TFLOPs"]},
+        "measured_peaks": mp,
     }
     print(json.dumps(res), flush=True)
 
@@ -278,8 +312,8 @@ def bench_bwd(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan14b-720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-blocks", type=int, default=360,
                     help="query blocks the CPU oracle baseline computes (0 = skip)")
@@ -383,6 +417,11 @@ def main():
     blended_peak = (i8 + bf) / t_roof_attn
     achieved = (i8 + bf) / (at_ms * 1e-3)
     traffic = traffic_entry() if args.qk == "int8" else None
+    mp = measured_peaks()
+    p_i8_m, p_bf_m = mp["int8_TOPs"] * 1e12, mp["bf16_TFLOPs"] * 1e12
+    blended_measured = (i8 + bf) / (i8 / p_i8_m + bf / p_bf_m)
+    t_roof_kept_m = (pairs * 2 * 64 * 64 * wl.d) / (p_i8_m if qk_int8 else p_bf_m) + \
+        (pairs * 2 * 64 * 64 * wl.d) / p_bf_m
 
     res = {
         "metric": METRIC,
@@ -402,7 +441,10 @@ def main():
                    "qk": args.qk},
         "ms_per_call": ms_step,
         "stage_ms": {"sla_quantize": q_ms, "sla_prepare_kv": kv_ms, "sla_attend": at_ms},
+        "ms_per_call_p10_median_p90": spread(st.sum(axis=1)),
+        "attend_ms_p10_median_p90": spread(st[:, 2]),
         "pct_mfma_roofline_kept_blocks": 100.0 * t_roof_kept / (ms_step * 1e-3),
+        "pct_mfma_roofline_kept_blocks_measured_peaks": 100.0 * t_roof_kept_m / (ms_step * 1e-3),
         "roofline": {
             "kernel": "k_attn (sla_attend)",
             "bound": "mfma",
@@ -411,7 +453,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / blended_peak,
             "traffic": traffic,
+            "peak_measured": blended_measured / 1e12,
+            "frac_of_measured": achieved / blended_measured,
         },
+        "measured_peaks": mp,
     }
     if args.cpu_blocks > 0:
         log("[bench] CPU oracle baseline")

@@ -1,4 +1,6 @@
-"""Build libsagesla.so for gfx950 in-tree with hipcc.
+"""Build libsagesla.so (the attention library) and libslapeak.so (the
+matrix-core peak measurement kernels the benchmark quotes fractions against)
+for gfx950 in-tree with hipcc.
 
     python -m sparse_bit_attention_amd.build
 """
@@ -13,12 +15,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsagesla.so")
+PEAK_OUT = os.path.join(PKG, "libslapeak.so")
 OBJ = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip", "k_bwd.hip",
            "sla_api.cpp"]
+PEAK_SOURCES = ["peak.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -35,8 +39,10 @@ FLAGS = [
 ]
 
 
-# Per-file extra hipcc flags (none at present; e.g. {"k_attn.hip": [...]}).
-EXTRA = {}
+# Per-file extra hipcc flags.  peak.hip: MFMA accumulators in ordinary
+# VGPRs (in AGPRs the compiler rotates the independent chains through
+# register copies every iteration, which the measurement must not contain).
+EXTRA = {"peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
@@ -50,18 +56,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + len(PEAK_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PEAK_SOURCES))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PEAK_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", PEAK_OUT)
     return OUT
 
 

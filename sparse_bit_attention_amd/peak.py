@@ -1,0 +1,105 @@
+"""Measured peaks of the GPU the benchmark runs on: matrix-core rates from
+kernels that do nothing but MFMAs (libslapeak.so, built from csrc/peak.hip)
+and the HBM rate of a plain device copy.  They are the practical ceilings a
+roofline fraction is also quoted against, beside the published peaks."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libslapeak.so")
+
+# kind -> (instruction, operand type); the 16x16 and 32x32 forms of each type
+KINDS = {
+    0: ("v_mfma_i32_16x16x64_i8", "int8"),
+    1: ("v_mfma_i32_32x32x32_i8", "int8"),
+    2: ("v_mfma_f32_16x16x32_bf16", "bf16"),
+    3: ("v_mfma_f32_32x32x16_bf16", "bf16"),
+}
+PUBLISHED = {"int8": 5.0e15, "bf16": 2.5e15}
+WAVES_PER_SIMD = 8  # workgroups of 4 waves, 8 per compute unit
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m sparse_bit_attention_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.slapeak_mfma.restype = ctypes.c_int
+        L.slapeak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+        L.slapeak_mfma_ops.restype = ctypes.c_longlong
+        L.slapeak_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def ops_per_launch(kind: int, iters: int, grid: int) -> int:
+    n = lib().slapeak_mfma_ops(kind, iters, grid)
+    if n < 0:
+        raise ValueError(f"bad peak kernel arguments kind={kind} iters={iters} grid={grid}")
+    return n
+
+
+def mfma_rate(kind: int, target_ms: float = 25.0, reps: int = 3) -> float:
+    """Best of `reps` timed launches of one MFMA kind, in ops (flops) per
+    second; each launch is sized to last about target_ms at the published
+    peak, with 8 waves on every SIMD."""
+    import torch
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid = cus * WAVES_PER_SIMD
+    per_iter = ops_per_launch(kind, 1, grid)
+    iters = max(1, int(target_ms * 1e-3 * PUBLISHED[KINDS[kind][1]] / per_iter))
+    out = torch.empty(grid * 4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    L = lib()
+
+    def launch():
+        rc = L.slapeak_mfma(kind, iters, grid, ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"slapeak_mfma(kind={kind}) failed with {rc}")
+
+    launch()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    return ops_per_launch(kind, iters, grid) / best
+
+
+def copy_rate(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """HBM bytes per second (read + write) of a plain device-to-device copy."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+
+
+def measure() -> dict:
+    """Measured peaks: the rate of each MFMA kind, the best of each operand
+    type (ops or flops per second) and the copy rate (bytes per second)."""
+    rates = {k: mfma_rate(k) for k in KINDS}
+    res = {"mfma": {KINDS[k][0]: r for k, r in rates.items()}}
+    for typ in ("int8", "bf16"):
+        res[typ] = max(r for k, r in rates.items() if KINDS[k][1] == typ)
+    res["hbm_copy"] = copy_rate()
+    return res
