@@ -280,6 +280,62 @@ struct QKOps {
     if constexpr (QK8) return mfma_i8(k, q, c);
     else return mfma_bf16(k, q, c);
   }
+  // Whether the pipelined loop writes its scores with mma_first / mma_next
+  // below in their VG form: d = 128 (the fine-scale path keeps the builtins:
+  // its key scales leave no VGPRs for the scores).  At d = 64 the compiler
+  // re-materialises the initial-value registers within a few instructions of
+  // an asm MFMA reading them, a distance the asm's hidden latency does not
+  // allow for.
+  static constexpr bool VG = D == 128;
+  // VG: the same products written as inline asm with VGPR operands, so the
+  // scores land in VGPRs whatever register class the compiler gives the
+  // function's other MFMA results.  With the builtins the whole kernel's
+  // MFMAs take the AGPR form (it needs more than 256 registers) and every
+  // score the vector ALU reads costs a v_accvgpr_read first: 128 extra
+  // instructions per two kept blocks, ~5% of the loop's time.  Every score
+  // tile of a loop must be written this way (mixing forms makes the compiler
+  // copy results between register classes right after the MFMA).
+  // The compiler cannot see the latency of an asm MFMA, so nothing may read
+  // its destination within the MFMA's result latency; the fixed slot order
+  // of the pipelined loop puts every such read a sub-stage later (dozens of
+  // instructions), and a test compiles this file and checks the distances
+  // on the generated code.  Accumulating into the same registers (exact
+  // srcC overlap) needs no wait.
+  // c0: the tile's initial value (init()); in the VG form a value the
+  // compiler cannot re-materialise (see opaque_init), so it stays in one set
+  // of registers for the whole loop instead of being rewritten next to the
+  // MFMAs that read it.
+  template <bool VG>
+  static __device__ __forceinline__ acc mma_first(const frag &k, const frag &q, const acc &c0) {
+    if constexpr (VG) {
+      acc r;
+      if constexpr (QK8)
+        asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %3" : "=&v"(r) : "v"(k), "v"(q), "v"(c0));
+      else
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %3" : "=&v"(r) : "v"(k), "v"(q), "v"(c0));
+      return r;
+    } else {
+      return mma(k, q, c0);
+    }
+  }
+  static __device__ __forceinline__ acc opaque_init() {
+    acc c = init();
+    asm volatile("" : "+v"(c));
+    return c;
+  }
+  template <bool VG>
+  static __device__ __forceinline__ acc mma_next(const frag &k, const frag &q, const acc &c) {
+    if constexpr (VG) {
+      acc r = c;
+      if constexpr (QK8)
+        asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(r) : "v"(k), "v"(q));
+      else
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(r) : "v"(k), "v"(q));
+      return r;
+    } else {
+      return mma(k, q, c);
+    }
+  }
   // the score as the float the exp2 argument is formed from
   static __device__ __forceinline__ float score(const acc &s, int r) {
     if constexpr (QK8) return __int_as_float(s[r]);
@@ -318,6 +374,7 @@ struct PipeState {
   v4f o[CG][4];
   v4f lacc[4];                   // row sums (every element of lacc[u] holds the same sum)
   typename Q::acc s[2][4];       // S^T of the two most recent tiles (by tile parity)
+  typename Q::acc s0;            // a score tile's initial value
   v4u pf[2][4];                  // B fragments of the two most recent 32-key chunks
   typename Q::frag kr[8][KC];    // K tiles (by tile index mod 8)
   v4u vr[8][VQ];                 // V quarters (by quarter index mod 8)
@@ -365,9 +422,6 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
   // SM(sigma): tile parity R & 1 fills half of chunk sigma/2's B fragment;
   // PV: chunk sigma/2 - 1, channel tiles [VQ (R&1), VQ (R&1) + VQ), V quarter
   // sigma-2.
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    st.s[(R + 1) & 1][u] = Q::init();
   constexpr int blk = R / 4;
   constexpr int par = (R / 2) & 1;         // chunk being filled by SM
   constexpr int par2 = ((R / 2) + 1) & 1;  // chunk consumed by PV
@@ -401,7 +455,12 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
       // no MFMA left in this slot
     } else if (i < 4 * KC) {
       const int kc = i / 4, u = i % 4;
-      st.s[(R + 1) & 1][u] = Q::mma(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
+      if (kc == 0)
+        st.s[(R + 1) & 1][u] =
+            Q::template mma_first<Q::VG && !FINE>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s0);
+      else
+        st.s[(R + 1) & 1][u] =
+            Q::template mma_next<Q::VG && !FINE>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
     } else if (i < 4 * KC + 4 * VQ) {
       const int j = i - 4 * KC, a = j / 4, u = j % 4;
       st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par2][u], st.o[a0 + a][u]);
@@ -472,6 +531,7 @@ __device__ __forceinline__ void kept_loop_piped(
   }
 
   PipeState<D, QK8> st;
+  st.s0 = Q::VG && !FINE ? Q::opaque_init() : Q::init();
 #pragma unroll
   for (int a = 0; a < CG; ++a)
 #pragma unroll
@@ -505,9 +565,10 @@ __device__ __forceinline__ void kept_loop_piped(
   // QK(0)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    typename Q::acc acc = Q::init();
+    typename Q::acc acc = Q::template mma_first<Q::VG && !FINE>(st.kr[0][0], qf[u][0], st.s0);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) acc = Q::mma(st.kr[0][kc], qf[u][kc], acc);
+    for (int kc = 1; kc < KC; ++kc)
+      acc = Q::template mma_next<Q::VG && !FINE>(st.kr[0][kc], qf[u][kc], acc);
     st.s[0][u] = acc;
   }
 
