@@ -79,10 +79,12 @@ def traffic_entry():
     return t.get("bytes_per_launch")
 
 
-def measured_peaks():
+def measured_peaks(skip=False):
     """The GPU's own ceilings, measured after the timed region: MFMA-only
     kernels per operand type (best of the 16x16 and 32x32 forms) and a plain
-    device copy.  Returned in the units the JSON line uses."""
+    device copy.  Returned in the units the JSON line uses; None if skipped."""
+    if skip:
+        return None
     from sparse_bit_attention_amd import peak
     r = peak.measure()
     return {
@@ -182,7 +184,7 @@ def bench_w8a8(args, dev):
     g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     ops = 2.0 * lw.M * lw.N * lw.K
     log(f"[bench] ms/step {ms_step:.3f} (quantize X {q_ms:.3f}, gemm {g_ms:.3f})")
-    mp = measured_peaks()
+    mp = measured_peaks(args.no_peaks)
     res = {
         "metric": "W8A8 block-128 linear layer TOPS (INT8 MFMA), Wan-14B-720P projection shape",
         "value": ops / (ms_step * 1e-3) / 1e12,
@@ -196,8 +198,8 @@ def bench_w8a8(args, dev):
         "roofline": {"kernel": "k_w8a8_gemm", "bound": "mfma", "achieved": ops / (g_ms * 1e-3) / 1e12,
                      "peak": P_I8 / 1e12, "unit": "TOP/s",
                      "frac": ops / (g_ms * 1e-3) / P_I8, "traffic": None,
-                     "peak_measured": mp["int8_TOPs"],
-                     "frac_of_measured": ops / (g_ms * 1e-3) / 1e12 / mp["int8_TOPs"]},
+                     "peak_measured": mp and mp["int8_TOPs"],
+                     "frac_of_measured": mp and ops / (g_ms * 1e-3) / 1e12 / mp["int8_TOPs"]},
         "measured_peaks": mp,
     }
     if args.cpu_blocks > 0:
@@ -287,7 +289,7 @@ def bench_bwd(args, dev):
     log(f"[bench] ms/step {ms_step:.3f} (forward {f_ms:.3f}, backward {b_ms:.3f})")
     dense = 10.0 * wl.B * wl.H * wl.N * wl.N * wl.d
     flops = bwd_work(wl, T, kb)
-    mp = measured_peaks()
+    mp = measured_peaks(args.no_peaks)
     res = {
         "metric": "SLA backward (bf16 QK^T, block mask fixed), dense-equivalent TFLOP/s",
         "value": dense / (b_ms * 1e-3) / 1e12,
@@ -302,8 +304,8 @@ def bench_bwd(args, dev):
         "roofline": {"kernel": "sla_attention_bwd (all backward kernels)", "bound": "mfma",
                      "achieved": flops / (b_ms * 1e-3) / 1e12, "peak": P_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": flops / (b_ms * 1e-3) / P_BF16, "traffic": None,
-                     "peak_measured": mp["bf16_TFLOPs"],
-                     "frac_of_measured": flops / (b_ms * 1e-3) / 1e12 / mp["bf16_TFLOPs"]},
+                     "peak_measured": mp and mp["bf16_TFLOPs"],
+                     "frac_of_measured": mp and flops / (b_ms * 1e-3) / 1e12 / mp["bf16_TFLOPs"]},
         "measured_peaks": mp,
     }
     print(json.dumps(res), flush=True)
@@ -325,6 +327,8 @@ def main():
                     help="sagesla: the attention forward (default); w8a8: the W8A8 linear layer; "
                          "bwd: plain-SLA forward + backward (training pair)")
     ap.add_argument("--linear", default="wan14b-720p-qkv", choices=sorted(synth.LINEAR_WORKLOADS))
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured peaks (profiled runs: keeps their kernels out of the trace)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -417,11 +421,13 @@ def main():
     blended_peak = (i8 + bf) / t_roof_attn
     achieved = (i8 + bf) / (at_ms * 1e-3)
     traffic = traffic_entry() if args.qk == "int8" else None
-    mp = measured_peaks()
-    p_i8_m, p_bf_m = mp["int8_TOPs"] * 1e12, mp["bf16_TFLOPs"] * 1e12
-    blended_measured = (i8 + bf) / (i8 / p_i8_m + bf / p_bf_m)
-    t_roof_kept_m = (pairs * 2 * 64 * 64 * wl.d) / (p_i8_m if qk_int8 else p_bf_m) + \
-        (pairs * 2 * 64 * 64 * wl.d) / p_bf_m
+    mp = measured_peaks(args.no_peaks)
+    blended_measured = t_roof_kept_m = None
+    if mp:
+        p_i8_m, p_bf_m = mp["int8_TOPs"] * 1e12, mp["bf16_TFLOPs"] * 1e12
+        blended_measured = (i8 + bf) / (i8 / p_i8_m + bf / p_bf_m)
+        t_roof_kept_m = (pairs * 2 * 64 * 64 * wl.d) / (p_i8_m if qk_int8 else p_bf_m) + \
+            (pairs * 2 * 64 * 64 * wl.d) / p_bf_m
 
     res = {
         "metric": METRIC,
@@ -444,7 +450,8 @@ def main():
         "ms_per_call_p10_median_p90": spread(st.sum(axis=1)),
         "attend_ms_p10_median_p90": spread(st[:, 2]),
         "pct_mfma_roofline_kept_blocks": 100.0 * t_roof_kept / (ms_step * 1e-3),
-        "pct_mfma_roofline_kept_blocks_measured_peaks": 100.0 * t_roof_kept_m / (ms_step * 1e-3),
+        "pct_mfma_roofline_kept_blocks_measured_peaks":
+            mp and 100.0 * t_roof_kept_m / (ms_step * 1e-3),
         "roofline": {
             "kernel": "k_attn (sla_attend)",
             "bound": "mfma",
@@ -453,8 +460,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / blended_peak,
             "traffic": traffic,
-            "peak_measured": blended_measured / 1e12,
-            "frac_of_measured": achieved / blended_measured,
+            "peak_measured": mp and blended_measured / 1e12,
+            "frac_of_measured": mp and achieved / blended_measured,
         },
         "measured_peaks": mp,
     }
