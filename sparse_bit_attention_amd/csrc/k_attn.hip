@@ -281,11 +281,9 @@ struct QKOps {
     else return mfma_bf16(k, q, c);
   }
   // Whether the pipelined loop writes its scores with mma_first / mma_next
-  // below in their VG form: d = 128 (the fine-scale path keeps the builtins:
-  // its key scales leave no VGPRs for the scores).  At d = 64 the compiler
-  // re-materialises the initial-value registers within a few instructions of
-  // an asm MFMA reading them, a distance the asm's hidden latency does not
-  // allow for.
+  // below in their VG form: d = 128.  At d = 64 the compiler re-materialises
+  // the initial-value registers within a few instructions of an asm MFMA
+  // reading them, a distance the asm's hidden latency does not allow for.
   static constexpr bool VG = D == 128;
   // VG: the same products written as inline asm with VGPR operands, so the
   // scores land in VGPRs whatever register class the compiler gives the
@@ -353,11 +351,12 @@ struct Pipe {
   static constexpr int VQ = CG / 2;      // 1 KiB fragments per V quarter
   // K tile sigma + KLEAD and V quarter sigma + VLEAD are loaded at sub-stage
   // sigma; bf16 Q and K fragments take twice the registers of INT8 ones, so
-  // that path keeps shorter rings.  INT8: a K ring of 3 leaves the fine-scale
-  // path's per-lane key scales room in the register file (4 spills) and
-  // saves the block-scale path a few accumulator copies (1.6% faster than 4).
-  static constexpr int KLEAD = QK8 ? 3 : 2;
-  static constexpr int VLEAD = QK8 ? 4 : 2;
+  // that path keeps shorter rings.  INT8 block scales: K 3 ahead saves a few
+  // accumulator copies (1.6% faster than 4).  Fine scales: the per-lane key
+  // scales and the VGPR score tiles fit the register file with K 2 and V 3
+  // ahead (K 3 / V 3 spills; K 2 / V 2 is 0.8% slower).
+  static constexpr int KLEAD = QK8 ? (FINE ? 2 : 3) : 2;
+  static constexpr int VLEAD = QK8 ? (FINE ? 3 : 4) : 2;
 };
 
 // Probabilities: p = exp2(score * c + nm) cut to bf16 by keeping the upper
@@ -457,10 +456,10 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
       const int kc = i / 4, u = i % 4;
       if (kc == 0)
         st.s[(R + 1) & 1][u] =
-            Q::template mma_first<Q::VG && !FINE>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s0);
+            Q::template mma_first<Q::VG>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s0);
       else
         st.s[(R + 1) & 1][u] =
-            Q::template mma_next<Q::VG && !FINE>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
+            Q::template mma_next<Q::VG>(st.kr[(R + 1) % 8][kc], qf[u][kc], st.s[(R + 1) & 1][u]);
     } else if (i < 4 * KC + 4 * VQ) {
       const int j = i - 4 * KC, a = j / 4, u = j % 4;
       st.o[a0 + a][u] = mfma_bf16(st.vr[vs][a], st.pf[par2][u], st.o[a0 + a][u]);
@@ -531,7 +530,7 @@ __device__ __forceinline__ void kept_loop_piped(
   }
 
   PipeState<D, QK8> st;
-  st.s0 = Q::VG && !FINE ? Q::opaque_init() : Q::init();
+  st.s0 = Q::VG ? Q::opaque_init() : Q::init();
 #pragma unroll
   for (int a = 0; a < CG; ++a)
 #pragma unroll
@@ -565,10 +564,10 @@ __device__ __forceinline__ void kept_loop_piped(
   // QK(0)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    typename Q::acc acc = Q::template mma_first<Q::VG && !FINE>(st.kr[0][0], qf[u][0], st.s0);
+    typename Q::acc acc = Q::template mma_first<Q::VG>(st.kr[0][0], qf[u][0], st.s0);
 #pragma unroll
     for (int kc = 1; kc < KC; ++kc)
-      acc = Q::template mma_next<Q::VG && !FINE>(st.kr[0][kc], qf[u][kc], acc);
+      acc = Q::template mma_next<Q::VG>(st.kr[0][kc], qf[u][kc], acc);
     st.s[0][u] = acc;
   }
 
