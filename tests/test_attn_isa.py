@@ -186,14 +186,24 @@ def isa(tmp_path_factory):
     return parse(out)
 
 
+# the d = 128 pipelined (bound-path) instances, mangled: k_attn<128, LIN, true, QK8, FINE>
+HOT = ["_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb0E", "_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb1E",
+       "_ZN3sla6k_attnILi128ELb1ELb1ELb0ELb0E", "_ZN3sla6k_attnILi128ELb0ELb1ELb1ELb0E"]
+
+
 def test_asm_mfma_results_are_not_read_early(isa):
     total = 0
     problems = []
+    per_kernel = {}
     for name, (ins, labels) in isa.items():
         n, bad = violations(ins, labels)
         total += n
+        per_kernel[name] = n
         problems += [(name[:60],) + b for b in bad[:3]]
     assert total > 0, "no inline-asm MFMA found: the check no longer covers the kernel"
+    for h in HOT:
+        found = [n for k, n in per_kernel.items() if k.startswith(h)]
+        assert found and found[0] > 0, f"{h}: the score products are no longer inline asm"
     assert not problems, "\n".join(map(str, problems))
 
 
