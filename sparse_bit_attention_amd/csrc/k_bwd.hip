@@ -624,13 +624,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
   // Q and dO double buffers (swizzled tiles of 64 D elements)
   constexpr int ST = 64 * D;
   __shared__ __attribute__((aligned(16))) uint16_t ra[4 * ST];
-  __shared__ float sl[2][64], sd[2][64];
+  __shared__ __attribute__((aligned(16))) float sl[2][64];
+  __shared__ __attribute__((aligned(16))) float sd[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int kblk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = kblk / T, j = kblk - bh * T;
   const int nj = min(BLK, N - j * BLK);
   const size_t rowbase = (size_t)bh * N + (size_t)j * BLK;
   const int s = 16 * w + l16;  // this lane column's key
+  // padding keys: P = 0 through a factor (a per-element condition on the
+  // exp2 becomes divergent branches that split the loop's schedule); the
+  // exp2 argument is always finite (padding keys' K rows are zero, padding
+  // queries' normaliser is +inf)
+  const float pkeep = s < nj ? 1.f : 0.f;
 
   // K and V fragments of the wave's 16 keys (B operands, k = channel)
   v4u kf[KC32], vf[KC32];
@@ -718,12 +724,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
       for (int h = 0; h < 2; ++h) {
         const int t = 2 * kc2 + h;
         float pv[4], dv4[4];
+        // query rows 16t + 4g .. +3: one 16-byte read each
+        const float4 l4 = *(const float4 *)&sl[buf][16 * t + 4 * g];
+        const float4 d4 = *(const float4 *)&sd[buf][16 * t + 4 * g];
+        const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qr = 16 * t + 4 * g + r;
-          pv[r] = s < nj ? __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][r], qk_scale, -sl[buf][qr]))
-                         : 0.f;  // padding keys: never stored, kept finite
-          dv4[r] = pv[r] * (dp[t][r] - sd[buf][qr]);
+          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[t][r], qk_scale, -lr[r])) * pkeep;
+          dv4[r] = pv[r] * (dp[t][r] - dr[r]);
         }
         pp[2 * h] = pack2bf(pv[0], pv[1]);
         pp[2 * h + 1] = pack2bf(pv[2], pv[3]);
