@@ -281,11 +281,11 @@ struct QKOps {
     else return mfma_bf16(k, q, c);
   }
   // Whether the pipelined loop writes its scores with mma_first / mma_next
-  // below in their VG form: d = 128.  At d = 64 the compiler re-materialises
+  // below in their ASM form: d = 128.  At d = 64 the compiler re-materialises
   // the initial-value registers within a few instructions of an asm MFMA
   // reading them, a distance the asm's hidden latency does not allow for.
   static constexpr bool VG = D == 128;
-  // VG: the same products written as inline asm with VGPR operands, so the
+  // ASM: the same products written as inline asm with VGPR operands, so the
   // scores land in VGPRs whatever register class the compiler gives the
   // function's other MFMA results.  With the builtins the whole kernel's
   // MFMAs take the AGPR form (it needs more than 256 registers) and every
@@ -299,13 +299,13 @@ struct QKOps {
   // instructions), and a test compiles this file and checks the distances
   // on the generated code.  Accumulating into the same registers (exact
   // srcC overlap) needs no wait.
-  // c0: the tile's initial value (init()); in the VG form a value the
+  // c0: the tile's initial value (init()); in the ASM form a value the
   // compiler cannot re-materialise (see opaque_init), so it stays in one set
   // of registers for the whole loop instead of being rewritten next to the
   // MFMAs that read it.
-  template <bool VG>
+  template <bool ASM>
   static __device__ __forceinline__ acc mma_first(const frag &k, const frag &q, const acc &c0) {
-    if constexpr (VG) {
+    if constexpr (ASM) {
       acc r;
       if constexpr (QK8)
         asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %3" : "=&v"(r) : "v"(k), "v"(q), "v"(c0));
@@ -321,9 +321,9 @@ struct QKOps {
     asm volatile("" : "+v"(c));
     return c;
   }
-  template <bool VG>
+  template <bool ASM>
   static __device__ __forceinline__ acc mma_next(const frag &k, const frag &q, const acc &c) {
-    if constexpr (VG) {
+    if constexpr (ASM) {
       acc r = c;
       if constexpr (QK8)
         asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(r) : "v"(k), "v"(q));
