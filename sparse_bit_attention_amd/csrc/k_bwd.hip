@@ -469,6 +469,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
       v4f s[4], dp[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = dp[t] = v4f{0.f, 0.f, 0.f, 0.f};
+      // raised wave priority around each block of products, so the other
+      // workgroup's wave on this SIMD does its vector and LDS work meanwhile
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kc = 0; kc < KC32; ++kc)
 #pragma unroll
@@ -476,6 +479,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
           s[t] = mfma_bf16(sw_rows<D>(sk, 16 * t, kc, lane), qf[kc], s[t]);
           dp[t] = mfma_bf16(sw_rows<D>(sv, 16 * t, kc, lane), of[kc], dp[t]);
         }
+      __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T (dP^T - D) in the key order of lds_frag (kmaj)
       v4u dsb[2];
 #pragma unroll
@@ -497,10 +501,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
         }
         dsb[kc2] = v4u{pk[0], pk[1], pk[2], pk[3]};
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
         for (int x = 0; x < CG; ++x) adq[x] = mfma_bf16(sw_frag<D>(sk, kc2, 16 * x, lane), dsb[kc2], adq[x]);
+      __builtin_amdgcn_s_setprio(0);
       if (n + 1 < kb) {
         tile_store_sw<D>(rk, ra + 2 * (cur ^ 1) * ST, tid);
         tile_store_sw<D>(rv, ra + (2 * (cur ^ 1) + 1) * ST, tid);
@@ -708,6 +714,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     v4f sa[4], dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) sa[t] = dp[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc = 0; kc < KC32; ++kc)
 #pragma unroll
@@ -715,6 +722,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
         sa[t] = mfma_bf16(sw_rows<D>(sq, 16 * t, kc, lane), kf[kc], sa[t]);
         dp[t] = mfma_bf16(sw_rows<D>(so, 16 * t, kc, lane), vf[kc], dp[t]);
       }
+    __builtin_amdgcn_s_setprio(0);
     // P and dS as B fragments in the query order of lds_frag
     v4u pb[2], dsb[2];
 #pragma unroll
@@ -742,6 +750,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
       dsb[kc2] = v4u{pd[0], pd[1], pd[2], pd[3]};
     }
     // dV^T += dO^T P, dK^T += Q^T dS: channel rows 16x + 4g + r, key column s
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
@@ -749,6 +758,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
         adv[x] = mfma_bf16(sw_frag<D>(so, kc2, 16 * x, lane), pb[kc2], adv[x]);
         adk[x] = mfma_bf16(sw_frag<D>(sq, kc2, 16 * x, lane), dsb[kc2], adk[x]);
       }
+    __builtin_amdgcn_s_setprio(0);
     if (inext >= 0) store_block(buf ^ 1);
     __syncthreads();
     buf ^= 1;

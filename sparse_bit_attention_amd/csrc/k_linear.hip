@@ -347,7 +347,12 @@ __global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict_
       load_words((s + 2) >> 1, wdn);
       read_b(smem + 1024 * b1, bf1);
       __builtin_amdgcn_sched_barrier(0);
+      // a wave issuing its products outranks the other wave of its SIMD, so
+      // the two drift apart and one's LDS and vector work runs under the
+      // other's MFMAs (s_setprio: wave priority only; ~2% here)
+      __builtin_amdgcn_s_setprio(1);
       mma_step(s, wdc, bf0);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       store_b(gA, smem + 1024 * b2);
       __syncthreads();
@@ -358,7 +363,9 @@ __global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict_
       load_b(s + 4, gA);
       read_b(smem + 1024 * b1, bf0);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       mma_step(s + 1, wdc, bf1);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       store_b(gB, smem + 1024 * b2);
       __syncthreads();

@@ -188,6 +188,10 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
     // while the matrix core computes the next tile.
     const float sc = sx[(size_t)mb * KB + kb] * sw[(size_t)nb * KB + kb];
     v4i ia[2];
+    // raised wave priority while this wave issues its products and folds:
+    // the other wave of the SIMD does its LDS reads and staging meanwhile
+    // instead of in lockstep (4% faster)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t <= 16; ++t) {
       if (t < 16) {
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (kb + 1 < KB) W8_LSTORE(s ^ 1)
     __syncthreads();
   }
