@@ -824,11 +824,27 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   // ||k_s||, so logit <= dq sm_scale log2(e) ||q_r|| max_j max_s (dk_s ||k_s||)
   // (INT8: codes and scales, dk per block or per key group; bf16: dq = dk = 1,
   // with a margin for the float32 sums of the products and norms).
+  // INT8: one kept entry per lane and a wave max (a serial walk of the list
+  // waits for two dependent scalar loads per kept block); the bf16 path keeps
+  // the walk (with the wave form its register allocation puts an operand
+  // copy right before an inline-asm MFMA)
   float kmax = 0.f, dkmax = 0.f;
-  for (int n = 0; n < kb; ++n) {
-    const int jj = kl[n];
-    kmax = fmaxf(kmax, dkn[headblk + jj]);
-    if (QK8) dkmax = fmaxf(dkmax, dkx[headblk + jj]);
+  if constexpr (QK8) {
+    for (int n0 = 0; n0 < kb; n0 += 64) {
+      const int n = n0 + lane;
+      if (n < kb) {
+        const int jj = kl[n];
+        kmax = fmaxf(kmax, dkn[headblk + jj]);
+        dkmax = fmaxf(dkmax, dkx[headblk + jj]);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
+      dkmax = fmaxf(dkmax, __shfl_xor(dkmax, off, 64));
+    }
+  } else {
+    for (int n = 0; n < kb; ++n) kmax = fmaxf(kmax, dkn[headblk + kl[n]]);
   }
   const float dqmax = fmaxf(fmaxf(dqi[0], dqi[1]), fmaxf(dqi[2], dqi[3]));
   bool bounded = !QK8 || dqmax * dkmax <= BIAS_C_LIMIT;
