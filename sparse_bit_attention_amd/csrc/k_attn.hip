@@ -795,6 +795,19 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   const int g = lane >> 4, l16 = lane & 15;
   const int nlast = N - (T - 1) * BLK;
 
+  // bf16: the largest key norm over the kept list (one entry per lane and a
+  // wave max) before the Q fragments are loaded, so they are not live across
+  // it; the INT8 paths take it after the scales below
+  float kmax_bf = 0.f;
+  if constexpr (!QK8) {
+    const int32_t *klb = kept + (size_t)qb * kb;
+    for (int n0 = 0; n0 < kb; n0 += 64) {
+      const int n = n0 + lane;
+      if (n < kb) kmax_bf = fmaxf(kmax_bf, dkn[(size_t)bh * T + klb[n]]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) kmax_bf = fmaxf(kmax_bf, __shfl_xor(kmax_bf, off, 64));
+  }
   typename QKOps<D, QK8>::frag qf[4][KC];
   if constexpr (QK8) load_q8<D>(q8 + (size_t)qb * BLK * D, qf, lane);
   else load_qbf<D>(Q + (size_t)bh * N * D, i, N, qf, lane);
@@ -844,7 +857,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       dkmax = fmaxf(dkmax, __shfl_xor(dkmax, off, 64));
     }
   } else {
-    for (int n = 0; n < kb; ++n) kmax = fmaxf(kmax, dkn[headblk + kl[n]]);
+    kmax = kmax_bf;
   }
   const float dqmax = fmaxf(fmaxf(dqi[0], dqi[1]), fmaxf(dqi[2], dqi[3]));
   bool bounded = !QK8 || dqmax * dkmax <= BIAS_C_LIMIT;
