@@ -6,9 +6,9 @@
  * (sections "支柱一：低比特注意力加速 – SageAttention", "支柱二：稀疏线性注意力 – SLA":
  * INT8 attention with outlier smoothing; exact attention on the important
  * block interactions, ~90% sparse, plus a light linear-attention component;
- * the two stack) and "TurboDiffusion深度解析…" (sections 2.1, 2.2: top-k
- * sparse selection with sla_topk; linear complexity through a kernel-function
- * approximation).
+ * the two stack) and "TurboDiffusion跨模态：图文音视频多模态融合探索"
+ * (zizhi168.cn; sections 2.1, 2.2: top-k sparse selection with sla_topk; linear
+ * complexity through a kernel-function approximation).
  *
  * Operator, per head (b,h) of Q, K, V in [B,H,N,d] bf16, blocks of 64 rows:
  *   1. block means of Q and K (float32, rows summed in order);
@@ -122,8 +122,8 @@ sla_status sla_attend(sla_plan_t plan, const void *q, void *out, void *ws, size_
                       void *stream);
 
 /* Backward pass of plain SLA (the trainable operator: pages "揭秘TurboDiffusion…"
- * section "支柱二：稀疏线性注意力 – SLA" and "TurboDiffusion跨模态…" section
- * "SLA稀疏线性注意力": the sparse pattern and the linear component are
+ * section "支柱二：稀疏线性注意力 – SLA" and the aiho.net news report (量子位, 2025-12-26)
+ * section "2. SLA稀疏线性注意力": the sparse pattern and the linear component are
  * learned, so the operator is differentiated).  Gradients of sum(dout * out)
  * with the block mask held fixed (the top-k selection passes no gradient):
  *   sparse branch: dS = P (dP - rowsum(dout * O_sparse)), dQ = sm_scale dS K,
@@ -181,7 +181,7 @@ sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *de
 
 /* ---- W8A8 linear layers ------------------------------------------------------
  * Pages: "揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化" and
- * "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写": the linear layers
+ * the aiho.net news report (量子位, 2025-12-26) section "4. W8A8量化+底层算子重写": the linear layers
  * around attention (QKV and output projections) run with weights and
  * activations both INT8, quantised over 128 x 128 blocks.  Readings: the step-5
  * recipe per block (symmetric, scale = amax / 127, codes = round half to even

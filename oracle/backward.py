@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 What it computes: the gradients of trainable SLA (pages: "揭秘TurboDiffusion…"
 section "支柱二：稀疏线性注意力 – SLA", the sparse pattern and the linear
-component are learned; "TurboDiffusion跨模态…" section "SLA稀疏线性注意力")
+component are learned; aiho.net news report (量子位, 2025-12-26)
+section "2. SLA稀疏线性注意力")
 for one head, with the block mask held fixed (top-k selection is a discrete
 choice and passes no gradient).  The forward is the bf16-QK^T operator (plain
 SLA): per query block i, softmax attention over the rows of its kept key

@@ -11,11 +11,13 @@
  *    smoothing) and "支柱二：稀疏线性注意力 – SLA" (exact attention on the most
  *    important block interactions, ~90% sparsity, plus a light linear-attention
  *    component; the two stack into SageSLA);
- *  - "TurboDiffusion深度解析…" (zizhi168.cn), sections 2.1 (Top-K sparse
+ *  - "TurboDiffusion跨模态：图文音视频多模态融合探索" (zizhi168.cn),
+ *    sections 2.1 (Top-K sparse
  *    selection, sla_topk) and 2.2 (SLA via kernel-function approximation;
  *    sla_topk 0.05 / 0.1 / 0.15);
- *  - "TurboDiffusion跨模态…" (aiho.net), "SageAttention2++" (outlier
- *    smoothing, INT8) and "SLA稀疏线性注意力" (SLA stacks on low-bit attention).
+ *  - the aiho.net news report (量子位, 2025-12-26), sections
+ *    "1. SageAttention2++" (outlier smoothing, INT8) and "2. SLA稀疏线性注意力"
+ *    (SLA stacks on low-bit attention).
  * The pages fix the operator only in outline; every step below that they leave
  * open follows the reading stated next to it.
  *
@@ -404,7 +406,7 @@ void sla_ref_combine(const double *Os, const double *Ol, const uint16_t *W, int 
 
 /* ---------------------------------------------------------------------------
  * W8A8 linear layers ("揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化";
- * "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写"): weights and
+ * aiho.net news report (量子位, 2025-12-26) section "4. W8A8量化+底层算子重写"): weights and
  * activations both INT8, quantised over 128 x 128 blocks.  Readings: the
  * scale recipe of step 5 per block (symmetric, amax / 127, round half to
  * even, clamp to [-127, 127]; a block of zeros has scale 0 and zero codes);

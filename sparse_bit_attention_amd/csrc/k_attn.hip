@@ -4,7 +4,8 @@
 // (INT8 QK^T on the matrix units, outlier smoothing) and "支柱二：稀疏线性注意力 –
 // SLA" (exact attention only on the kept block interactions, a linear
 // component for the rest; sparse and low-bit computation stack as SageSLA);
-// "TurboDiffusion跨模态…" sections "SageAttention2++" and "SLA稀疏线性注意力".
+// the aiho.net news report (量子位, 2025-12-26) sections
+// "1. SageAttention2++" and "2. SLA稀疏线性注意力".
 //
 // One wave owns one 64-row query block and walks its kept key blocks in
 // ascending order:
@@ -35,9 +36,13 @@ namespace sla {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
-// Largest per-row logit bound (log2 units) for which exp2(logit - bound) keeps
-// the row's largest probabilities far from float32 underflow.
-constexpr float BOUND_LIMIT = 64.0f;
+// Largest per-row logit bound m (log2 units) the bound path accepts.  The
+// Cauchy-Schwarz bound holds on both sides, -m <= logit <= m, so every
+// probability exp2(logit - m) is at least 2^(-2m): with m <= 48 that is 2^-96,
+// which keeps each probability, the row sum and every P*V product far inside
+// the float32 normal range (2^-126) even when all of a row's kept logits sit
+// near -m.  Rows with a larger bound go to the online-max launch.
+constexpr float BOUND_LIMIT = 48.0f;
 
 template <int D>
 __device__ __forceinline__ void load_q8(const int8_t *q8blk, v4i (&qf)[4][D / 64], int lane) {

@@ -1,7 +1,8 @@
 // Backward pass of plain SLA (bf16 QK^T), the block mask held fixed.
 //
 // Pages: "揭秘TurboDiffusion…" section "支柱二：稀疏线性注意力 – SLA" and
-// "TurboDiffusion跨模态…" section "SLA稀疏线性注意力": SLA's sparse pattern and
+// the aiho.net news report (量子位, 2025-12-26) section
+// "2. SLA稀疏线性注意力": SLA's sparse pattern and
 // linear component are trained, so the operator is differentiated.  The top-k
 // selection is a discrete choice and passes no gradient.
 //

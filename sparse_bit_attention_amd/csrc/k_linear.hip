@@ -3,8 +3,8 @@
 //
 // Pages: "揭秘TurboDiffusion…" section "支柱二：稀疏线性注意力 – SLA" (a light
 // linear-attention component complements the sparse exact part);
-// "TurboDiffusion深度解析…" section 2.2 (linear complexity through a
-// kernel-function approximation).  The feature map phi is read as a softmax
+// "TurboDiffusion跨模态：图文音视频多模态融合探索" (zizhi168.cn) section 2.2
+// (linear complexity through a kernel-function approximation).  The feature map phi is read as a softmax
 // over the d channels of each raw K (and Q) row.
 //
 // k_kv_prep, one workgroup per key block j (memory bound: reads K_j and V_j,

@@ -2,8 +2,8 @@
 //
 // Pages: "揭秘TurboDiffusion…" section "支柱一：低比特注意力加速 – SageAttention"
 // (attention in INT8 with outlier smoothing) and section "支柱二：稀疏线性注意力 – SLA"
-// (block selection from pooled blocks); "TurboDiffusion跨模态…" section
-// "SageAttention2++" (outlier smoothing).  The float32 operation order below is
+// (block selection from pooled blocks); the aiho.net news report (量子位, 2025-12-26)
+// section "1. SageAttention2++" (outlier smoothing).  The float32 operation order below is
 // part of the operator's definition (block means feed an integer decision, the
 // top-k mask): sums run over the rows of a block in order, the K mean over the
 // blocks in order, divisions are done in float64 and rounded once.

@@ -1,7 +1,8 @@
 // Block scores and per-row top-k selection.
 //
-// Pages: "TurboDiffusion深度解析…" section 2.1 (Top-K sparse selection, sla_topk)
-// and section 2.2 (sla_topk 0.05 / 0.1 / 0.15); "揭秘TurboDiffusion…" section
+// Pages: "TurboDiffusion跨模态：图文音视频多模态融合探索" (zizhi168.cn)
+// section 2.1 (Top-K sparse selection, sla_topk) and section 2.2 (sla_topk
+// 0.05 / 0.1 / 0.15); "揭秘TurboDiffusion…" section
 // "支柱二：稀疏线性注意力 – SLA" (only the most important block interactions get
 // exact attention, ~90% sparsity).
 //

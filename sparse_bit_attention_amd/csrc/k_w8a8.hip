@@ -3,8 +3,8 @@
 //
 // Pages: "揭秘TurboDiffusion…" section "支柱三：W8A8线性层量化" (weights and
 // activations of the linear layers both INT8, quantised over 128 x 128
-// blocks) and "TurboDiffusion跨模态…" section "W8A8量化+底层算子重写" (the same,
-// run on the INT8 matrix units).
+// blocks) and the aiho.net news report (量子位, 2025-12-26)
+// section "4. W8A8量化+底层算子重写" (the same, run on the INT8 matrix units).
 //
 // k_quant_b128: one workgroup per 128 x 128 block of a bf16 [R][C] matrix:
 //   scale = amax / 127 (float64 division), codes = rint(x * float32(127 /

@@ -203,7 +203,11 @@ def sampled_compare(wl, heads, check_dw):
     dW = np.zeros((wl.d, wl.d))
     for b, h in heads:
         bh = b * wl.H + h
-        mask = masks[bh * T:(bh + 1) * T].astype(bool)
+        # the reference takes the oracle's own selection; the GPU plan's mask
+        # must equal it bit for bit before it is used
+        prep = oracle.head_prep(q[b, h], k[b, h], float(np.float32(wl.topk)))
+        assert np.array_equal(masks[bh * T:(bh + 1) * T], prep.mask), f"mask of head {(b, h)}"
+        mask = prep.mask.astype(bool)
         rq, rk, rv, rw = obwd.backward_sampled(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(w),
                                                f64(do[b, h]), mask, sc, qbl, kbl,
                                                bool(wl.use_linear))

@@ -183,6 +183,61 @@ def test_tied_block_scores(period):
     full_compare(wl, inputs=tied_inputs(wl, period))
 
 
+def anti_aligned_inputs(wl, beta, seed):
+    """Every query block keeps key blocks 0 .. T/2-1 (block means: channel 0
+    of Q is 1, of those keys +1, of the others -1).  Channel 1 alternates
+    +beta / -beta over the query rows, is -beta on the kept keys and +beta on
+    the others (so the K mean stays ~0): the even rows' logits over their
+    kept keys all sit near minus their Cauchy-Schwarz bound (about
+    0.1275 beta^2 in log2 units), the odd rows' near plus it."""
+    rng = np.random.default_rng(seed)
+    N, d = wl.N, wl.d
+    q = rng.standard_normal((N, d)) * 0.05
+    k = rng.standard_normal((N, d)) * 0.05
+    q[:, 0] = 1.0
+    q[:, 1] = np.where(np.arange(N) % 2 == 0, beta, -beta)
+    kept = np.arange(N) < 64 * (wl.T // 2)
+    k[:, 0] = np.where(kept, 1.0, -1.0)
+    k[:, 1] = np.where(kept, -beta, beta)
+    _, _, v, w = synth.all_inputs(wl)
+    return (synth.f64_to_bf16_bits(q).reshape(1, 1, N, d),
+            synth.f64_to_bf16_bits(k).reshape(1, 1, N, d), v, w)
+
+
+@pytest.mark.parametrize("qk", ["int8", "int8-fine", "bf16"])
+@pytest.mark.parametrize("beta", [17.75, 22.25])
+def test_rows_with_every_kept_logit_near_minus_the_bound(beta, qk):
+    """Rows whose kept logits all lie near -m, m their logit bound: with
+    beta = 17.75 (m ~ 40) they stay in the bound launch and their
+    probabilities are ~2^-80; with beta = 22.25 (m ~ 63, where 2^(-2m) would
+    leave the float32 normal range) they must go to the second launch.  Both
+    match the oracle."""
+    wl = synth.Workload(f"anti-aligned-{beta}", 1, 1, 512, 128, 0.5, use_linear=0, seed=21)
+    inputs = anti_aligned_inputs(wl, beta, seed=22)
+    prep = oracle.head_prep(inputs[0][0, 0], inputs[1][0, 0], 0.5)
+    assert np.array_equal(prep.kept, np.tile(np.arange(4), (wl.T, 1)))
+    full_compare(wl, inputs=inputs, qk_int8=qk != "bf16", fine=qk == "int8-fine")
+
+
+def test_kmean_block_order_hand_case():
+    """The hand case of tests/golden/hand_cases.json (kmean_order), scaled by
+    2^-20 (exact: no value becomes subnormal) so the logits stay moderate: the
+    K mean must be the block-order float32 sum of the block sums; a reversed
+    block order, a token-order or a float64 sum give different bits."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))["kmean_order"]
+    wl = synth.Workload("kmean-order", 1, 1, g["N"], 128, 0.5, seed=23)
+    q, _, v, w = synth.all_inputs(wl)
+    kf = np.zeros((wl.N, wl.d))
+    for r, val in g["rows_and_values"]:
+        kf[r, :] = val * 2.0 ** -20
+    k = synth.f64_to_bf16_bits(kf).reshape(1, 1, wl.N, wl.d)
+    m, o, dv, inputs = full_compare(wl, inputs=(q, k, v, w))
+    mu = m.region("MU")[0].cpu().numpy()
+    assert np.all(mu == np.float32(g["mu"] * 2.0 ** -20))
+
+
 def test_explicit_sm_scale():
     full_compare(synth.Workload("scale", 1, 1, 777, 128, 0.2, seed=9), sm_scale=0.05)
 
@@ -294,6 +349,44 @@ def test_full_size_sampled_parity(name):
         for n, (_, i, j) in enumerate(pairs):
             assert np.array_equal(tiles[n], oracle.qk_int32(prep.q8, prep.k8, i, j))
     assert_close(np.concatenate(G), np.concatenate(R), name)
+
+
+def test_dense_outlier_against_float64_dense_attention():
+    """The dense INT8 stress workload (topk 1, no linear branch, K offsets
+    ~N(0,16) with one channel x20) at full size against float64 dense softmax
+    attention of the same bf16 inputs (the oracle's exact-logit mode), on
+    sampled query blocks of two heads, with block scales and with fine scales.
+    This is an accuracy characterisation of INT8 QK^T, not the GPU-versus-
+    oracle bar: quantisation alone puts the output ~1.3e-2 (block scales) and
+    ~1.15e-2 (16-row / 4-key scales) from float64 in relative L2, the oracle's
+    analytic model and its own pin agree, and the assertion is that model's
+    bound (2e-2) plus max-abs 2e-2."""
+    wl = synth.WORKLOADS["dense-outlier"]
+    say(f"[gpu] generating {wl.name}")
+    inputs = synth.all_inputs(wl)
+    q, k, v, w = inputs
+    T = wl.T
+    blocks = [0, 1, T // 2, T - 1]
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    ref = []
+    for b, h in heads:
+        exact = oracle.head_forward(q[b, h], k[b, h], v[b, h], w, 1.0, use_linear=False,
+                                    blocks=blocks, qk_int8=False)
+        ref.append(np.concatenate([exact[i] for i in blocks]))
+    ref = np.concatenate(ref)
+    errs = {}
+    for fine in (False, True):
+        m, o, _, _ = run(wl, inputs=inputs, fine=fine)
+        out = host_u16(o)
+        got = np.concatenate([f32(out[b, h, 64 * i:64 * i + min(64, wl.N - 64 * i)])
+                              for b, h in heads for i in blocks])
+        mx = float(np.abs(got - ref).max())
+        errs[fine] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        say(f"[accuracy] dense-outlier vs float64 dense, {'fine' if fine else 'block'} scales: "
+            f"rel-L2 {errs[fine]:.3e} max-abs {mx:.3e}")
+        assert mx <= MAX_ABS and errs[fine] <= 2e-2
+        del m, o
+    assert errs[True] < errs[False]
 
 
 @pytest.mark.parametrize("name", ["wan14b-720p"])

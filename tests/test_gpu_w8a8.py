@@ -82,6 +82,28 @@ def test_w8a8_quant_ragged_columns_and_zero_block():
     assert rs[0, 0] == 0.0 and rs[0, 1] == 0.0  # the top row blocks are all zero
 
 
+def test_w8a8_gemm_fold_order_hand_case():
+    """The hand case of tests/golden/hand_cases.json (w8a8_fold): only the
+    ascending fused fold over the K blocks gives -2^-25 (a rounded product or
+    the descending order give 0)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))["w8a8_fold"]
+    K = g["K"]
+    xq = np.zeros((1, K), np.int8)
+    wq = np.zeros((1, K), np.int8)
+    for c, v in g["x_codes"]:
+        xq[0, c] = v
+    for c, v in g["w_codes"]:
+        wq[0, c] = v
+    y = sla.w8a8_gemm(torch.from_numpy(xq).cuda(), torch.tensor([g["sx"]], dtype=torch.float32).cuda(),
+                      torch.from_numpy(wq).cuda(), torch.tensor([g["sw"]], dtype=torch.float32).cuda())
+    torch.cuda.synchronize()
+    got = synth.bf16_bits_to_f32(host_u16(y))[0, 0]
+    say(f"[parity] w8a8 fold hand case: {got!r} (expected {g['y']!r})")
+    assert got == np.float32(g["y"])
+
+
 def test_w8a8_rejects_bad_k():
     xq = torch.zeros((4, 100), dtype=torch.int8, device="cuda")
     sx = torch.zeros((1, 1), dtype=torch.float32, device="cuda")

@@ -4,6 +4,7 @@ inputs, library routines (numpy / scipy) for the special cases the method
 reduces to, closed forms and invariants.  CPU only."""
 import json
 import math
+import pathlib
 import os
 
 import numpy as np
@@ -94,6 +95,23 @@ def test_kmean_is_token_mean():
     ref = x.mean(0)  # mean over the N valid tokens, not T*64
     bound = (N + 16) * EPS32 * np.abs(x).sum(0) / N * 1.01
     assert np.all(np.abs(mu - ref) <= bound)
+
+
+def test_kmean_block_order_hand_case():
+    """The float32 K mean sums the block sums in block order (hand case: a
+    reversed block order, a token-order sum or a float64 sum each give a
+    different float32 mean)."""
+    g = GOLD["kmean_order"]
+    N = g["N"]
+    mu = oracle.kmean(np.array(g["block_sums"], np.float32)[:, None], N)
+    assert mu[0] == np.float32(g["mu"])
+    K = np.zeros((N, 8))
+    for r, v in g["rows_and_values"]:
+        K[r, :] = v
+    ksum, _ = oracle.pool(bf16(K))
+    assert np.array_equal(ksum[:, 0], np.array(g["block_sums"], np.float32))
+    mu = oracle.kmean(ksum, N)
+    assert np.all(mu == np.float32(g["mu"]))
 
 
 # -------------------------------------------------------- block scores (S3) ---
@@ -451,6 +469,23 @@ def test_w8a8_gemm_hand_case():
     assert synth.bf16_bits_to_f32(y)[0, 0] == GOLD["w8a8_gemm"]["y"]
 
 
+def test_w8a8_gemm_fold_order_hand_case():
+    """One fused multiply-add per K block, ascending from +0 (hand case: a
+    rounded product or the descending order each give 0 instead of -2^-25)."""
+    g = GOLD["w8a8_fold"]
+    K = g["K"]
+    xq = np.zeros((1, K), np.int8)
+    wq = np.zeros((1, K), np.int8)
+    for c, v in g["x_codes"]:
+        xq[0, c] = v
+    for c, v in g["w_codes"]:
+        wq[0, c] = v
+    y32, y = oracle.w8a8_gemm(xq, np.array([g["sx"]], np.float32), wq,
+                              np.array([g["sw"]], np.float32))
+    assert y32[0, 0] == np.float32(g["y"])
+    assert synth.bf16_bits_to_f32(y)[0, 0] == np.float32(g["y"])
+
+
 def test_w8a8_gemm_unit_scales_is_integer_matmul():
     rng = np.random.default_rng(5)
     M, N, K = 70, 45, 384  # not square: a transposed operand would fail
@@ -637,19 +672,19 @@ def _bwd_problem(seed, N=150, d=8):
     return Q, K, V, W, dO, rng
 
 
-@pytest.mark.parametrize("mask_name", sorted(BWD_MASKS))
-@pytest.mark.parametrize("use_linear", [True, False])
-def test_backward_matches_central_differences(mask_name, use_linear):
-    """d/de sum(dO * O(X + e E)) at e = 0, by central differences of the
-    float64 forward, equals <dX, E> for random directions E in each of Q, K,
-    V, W, and single entries (ragged last block: N = 150)."""
+def _fd_mismatches(module, mask_name, use_linear):
+    """(central difference, analytic) directional derivatives of
+    sum(dO * O) for the backward of ``module``, the forward always taken from
+    the oracle itself."""
     Q, K, V, W, dO, rng = _bwd_problem(7 if use_linear else 8)
     mask = np.array(BWD_MASKS[mask_name], bool)
     sc = 0.35
-    g = bwd.backward(Q, K, V, W, dO, mask, sc, use_linear)
+    g = module.backward(Q, K, V, W, dO, mask, sc, use_linear)
 
     def loss(Q_, K_, V_, W_):
         return float(np.sum(dO * bwd.forward(Q_, K_, V_, W_, mask, sc, use_linear).O))
+
+    out = []
 
     args = [Q, K, V, W]
     grads = [g.dQ, g.dK, g.dV, g.dW]
@@ -671,9 +706,54 @@ def test_backward_matches_central_differences(mask_name, use_linear):
             xm[a] -= eps * E
             fd = (loss(*xp) - loss(*xm)) / (2 * eps)
             an = float(np.sum(grads[a] * E))
-            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (a, fd, an)
+            out.append((a, fd, an))
+    return out, g
+
+
+@pytest.mark.parametrize("mask_name", sorted(BWD_MASKS))
+@pytest.mark.parametrize("use_linear", [True, False])
+def test_backward_matches_central_differences(mask_name, use_linear):
+    """d/de sum(dO * O(X + e E)) at e = 0, by central differences of the
+    float64 forward, equals <dX, E> for random directions E in each of Q, K,
+    V, W, and single entries (ragged last block: N = 150)."""
+    pairs, g = _fd_mismatches(bwd, mask_name, use_linear)
+    for a, fd, an in pairs:
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (a, fd, an)
     if not use_linear:
         assert np.all(g.dW == 0)
+
+
+# Plausible mistakes planted in a copy of the backward oracle (never in the
+# oracle itself): each must be caught by the central-difference pin above on
+# at least one of its problems.
+BWD_MUTANTS = {
+    "sign of dden": ("dden = -(G[r] * Ol).sum(axis=1, keepdims=True) / den",
+                     "dden = (G[r] * Ol).sum(axis=1, keepdims=True) / den"),
+    "dropped D": ("dS = P * (dP - D)", "dS = P * dP"),
+    "transposed dHb": ("dV[rj] += B @ dHb", "dV[rj] += B @ dHb.T"),
+    "missing sm_scale in dQ": ("dQ[r] += sm_scale * dS @ K[s]", "dQ[r] += dS @ K[s]"),
+    "dropped dz": ("dB = V[rj] @ dHb.T + dzb[None, :]", "dB = V[rj] @ dHb.T"),
+    "dK from P instead of dS": ("np.add.at(dK, s, sm_scale * dS.T @ Q[r])",
+                                "np.add.at(dK, s, sm_scale * P.T @ Q[r])"),
+    "phi_grad sign": ("return A * (dA - (A * dA).sum(axis=1, keepdims=True))",
+                      "return A * (dA + (A * dA).sum(axis=1, keepdims=True))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_pins_catch_planted_mistakes(name):
+    import types
+    src = pathlib.Path(bwd.__file__).read_text()
+    old, new = BWD_MUTANTS[name]
+    assert old in src, name
+    mutant = types.ModuleType("backward_mutant")
+    exec(compile(src.replace(old, new, 1), "backward_mutant", "exec"), mutant.__dict__)
+    caught = False
+    for mask_name in sorted(BWD_MASKS):
+        for use_linear in (True, False):
+            pairs, _ = _fd_mismatches(mutant, mask_name, use_linear)
+            caught |= any(abs(fd - an) > 1e-7 * max(1.0, abs(fd)) for _, fd, an in pairs)
+    assert caught, name
 
 
 def test_backward_euler_identities():
