@@ -174,8 +174,11 @@ sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr,
 
 /* The int32 QK^T block products the attention kernel computes, for n pairs
  * given as int32 (bh, i, j) triples in device memory; dev_out receives n
- * tiles of int32 [64 query rows][64 key rows].  Uses the same device code as
- * the attention kernel.  Needs sla_quantize first and qk_int8 = 1. */
+ * tiles of int32 [64 query rows][64 key rows] (zeros for a triple out of
+ * range).  Runs the attention kernel's own bound-path loop, with kept list
+ * {j} for query block (bh, i), and stores each score accumulator (minus the
+ * loop's bias) where the softmax reads it; nothing else is written.  Needs
+ * sla_quantize first and qk_int8 = 1; n >= 0 (else SLA_EINVAL). */
 sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *dev_pairs, int32_t n,
                               int32_t *dev_out, void *stream);
 

@@ -53,22 +53,6 @@ __device__ __forceinline__ void load_q8(const int8_t *q8blk, v4i (&qf)[4][D / 64
     for (int kc = 0; kc < D / 64; ++kc) qf[u][kc] = p[(u * (D / 64) + kc) * 64 + lane];
 }
 
-// S^T tile (key tile t, query tile u) = sum over channel chunks of K8 x Q8.
-// Accumulator lane l, register r: key 16t + 4(l/16) + r, query 16u + l%16.
-template <int D>
-__device__ __forceinline__ void qk_int8(const v4i (&kf)[4][D / 64], const v4i (&qf)[4][D / 64],
-                                        v4i (&s)[4][4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v4i a = {0, 0, 0, 0};
-#pragma unroll
-      for (int kc = 0; kc < D / 64; ++kc) a = mfma_i8(kf[t][kc], qf[u][kc], a);
-      s[t][u] = a;
-    }
-}
-
 // One key block's operands, straight from HBM in register layout: the K8
 // fragments (A operands of S^T) and the V^T fragments of both 32-key halves
 // (A operands of O^T).
@@ -398,12 +382,16 @@ struct PipeBlocks {
 // Sub-stage R (0..7) of the loop body; sigma = 8 i + R.
 // lm[h]: the ones fragment for half h of the head's last block, zero at its
 // padding keys, so the row sums leave those keys out.
-template <int D, bool QK8, bool FINE, int R>
+// DUMP (INT8 only): also store each score of block 2i (R < 4) as the exact
+// int32 q.k sum, accumulator minus SCORE_BIAS_BITS, to dump[64 query][64 key]
+// at the slot where the softmax reads it.
+template <int D, bool QK8, bool FINE, int R, bool DUMP>
 __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
                                           const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK],
                                           const PipeBlocks &pb, const v4u (&lm)[2],
                                           const uint4 *kload_src, const uint4 *vload_src,
-                                          int lane) {
+                                          int lane, int32_t *dump) {
+  static_assert(!DUMP || QK8, "the int32 read-back exists for INT8 scores only");
   using P = Pipe<D, QK8, FINE>;
   using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, VQ = P::VQ;
@@ -495,6 +483,9 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
         x = __builtin_fmaf(Q::score(st.s[R & 1][u], r), cu[u], nmu[u]);
       }
       xs[u][r] = __float_as_uint(__builtin_amdgcn_exp2f(x));
+      if constexpr (DUMP && R < 4)
+        dump[(16 * u + (lane & 15)) * BLK + 16 * R + 4 * (lane >> 4) + r] =
+            st.s[R & 1][u][r] - SCORE_BIAS_BITS;
     }
     // tile pu's four probabilities are complete: pack them
     const int pu = SP ? (i >= 4 && i <= 16 && i % 4 == 0 ? i / 4 - 1 : -1)
@@ -521,12 +512,12 @@ __device__ __forceinline__ void sub_stage(PipeState<D, QK8> &st,
 // K fragments come from k8u (QK8: INT8 codes) or the bf16 copy (bfk_off).
 // dqi[u]: the query tile's scale factor (all equal unless FINE); FINE: dk
 // holds 16 scales per key block, this lane's keys of tile t use 4t + g.
-template <int D, bool QK8, bool FINE>
+template <int D, bool QK8, bool FINE, bool DUMP = false>
 __device__ __forceinline__ void kept_loop_piped(
     const typename QKOps<D, QK8>::frag (&qf)[4][QKOps<D, QK8>::NK], v4f (&o)[D / 16][4],
     const float (&m)[4], float (&lsum)[4], const int32_t *kl, int kb, const float *dk,
     const uint4 *k8u, const uint4 *vtu, size_t headblk, const float (&dqi)[4], int T, int nlast,
-    int lane) {
+    int lane, int32_t *dump = nullptr) {
   using P = Pipe<D, QK8, FINE>;
   using Q = QKOps<D, QK8>;
   constexpr int KC = P::KC, CG = P::CG, VQ = P::VQ, KT = P::KT;
@@ -662,7 +653,7 @@ __device__ __forceinline__ void kept_loop_piped(
 #define SLA_SRC(base, FR, PER, R, LEAD) \
     ((base) + ((headblk + jb[((R) + (LEAD)) >> 2]) * (FR) + (((R) + (LEAD)) & 3) * (PER)) * 64)
 #define SLA_SUB(R) \
-    sub_stage<D, QK8, FINE, R>(st, qf, pb, lm, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane)
+    sub_stage<D, QK8, FINE, R, DUMP>(st, qf, pb, lm, SLA_SRC(k8u, KFR, KT, R, P::KLEAD), SLA_SRC(vtu, VFR, VQ, R, P::VLEAD), lane, dump)
     SLA_SUB(0);
     SLA_SUB(1);
     SLA_SUB(2);
@@ -780,7 +771,13 @@ __device__ void exact_row_max(const v4u (&qf)[4][D / 32], const int32_t *kl, int
 // INT8 step, no scales; the logit scale is sm_scale alone).  FINE (INT8
 // only): one Q scale per 16 rows (dq [qb][4]) and one K' scale per 4 keys
 // (dk [block][16]).
-template <int D, bool LIN, bool BOUND, bool QK8, bool FINE>
+// DUMP (INT8, BOUND): the int32 read-back form.  Wave t takes the triple
+// (bh, i, j) = dpairs[3t .. 3t+2] (t < ndump; nqb stays the number of query
+// blocks) and runs query block bh*T + i through the same bound-path loop with
+// the one-entry kept list {j}, storing the loop's own score accumulators,
+// minus the bias, to dump[t][64 query][64 key] (zeros for a triple out of
+// range); nothing else is written.
+template <int D, bool LIN, bool BOUND, bool QK8, bool FINE, bool DUMP>
 __global__ __launch_bounds__(256, 1) void k_attn(
     const int8_t *__restrict__ q8, const void *__restrict__ kfr, const float *__restrict__ dq,
     const float *__restrict__ dk, const float *__restrict__ dkn, const float *__restrict__ dkx,
@@ -788,14 +785,38 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
     int32_t *__restrict__ flags, float *__restrict__ lse, uint16_t *__restrict__ os, int N, int T,
-    int kb, int nqb, int F, float qk_scale) {
+    int kb, int nqb, int F, float qk_scale, const int32_t *__restrict__ dpairs,
+    int32_t *__restrict__ dump, int ndump) {
+  static_assert(!DUMP || (QK8 && BOUND && !LIN), "read-back form: INT8 bound loop only");
   constexpr int CG = D / 16, KC32 = D / 32;
   constexpr int KC = QKOps<D, QK8>::NK;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-  if (qb >= nqb) return;  // no barriers below: waves are independent
-  if (!BOUND && flags[qb] == 0) return;
+  int qb;
+  const int32_t *kl;
+  int32_t *dmp = nullptr;
+  if constexpr (DUMP) {
+    const int t = blockIdx.x * 4 + w;
+    if (t >= ndump) return;  // no barriers below: waves are independent
+    const int bh0 = dpairs[3 * t], i0 = dpairs[3 * t + 1], j0 = dpairs[3 * t + 2];
+    dmp = dump + (size_t)t * BLK * BLK;
+    if (bh0 < 0 || bh0 >= nqb / T || i0 < 0 || i0 >= T || j0 < 0 || j0 >= T) {
+      for (int x = lane; x < BLK * BLK; x += 64) dmp[x] = 0;
+      return;
+    }
+    qb = bh0 * T + i0;
+    kl = dpairs + 3 * t + 2;
+    // a list length the compiler cannot see, so the loop keeps the
+    // production form (with a constant 1 it folds the loop and moves the
+    // first score reads next to the asm MFMAs that write them)
+    kb = 1;
+    asm volatile("" : "+s"(kb));
+  } else {
+    qb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
+    if (qb >= nqb) return;  // no barriers below: waves are independent
+    if (!BOUND && flags[qb] == 0) return;
+    kl = kept + (size_t)qb * kb;
+  }
   const int bh = qb / T, i = qb - bh * T;
   const int g = lane >> 4, l16 = lane & 15;
   const int nlast = N - (T - 1) * BLK;
@@ -805,10 +826,9 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   // it; the INT8 paths take it after the scales below
   float kmax_bf = 0.f;
   if constexpr (!QK8) {
-    const int32_t *klb = kept + (size_t)qb * kb;
     for (int n0 = 0; n0 < kb; n0 += 64) {
       const int n = n0 + lane;
-      if (n < kb) kmax_bf = fmaxf(kmax_bf, dkn[(size_t)bh * T + klb[n]]);
+      if (n < kb) kmax_bf = fmaxf(kmax_bf, dkn[(size_t)bh * T + kl[n]]);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) kmax_bf = fmaxf(kmax_bf, __shfl_xor(kmax_bf, off, 64));
@@ -829,7 +849,6 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     for (int u = 0; u < 4; ++u) o[a][u] = v4f{0.f, 0.f, 0.f, 0.f};
   float m[4], lsum[4];
 
-  const int32_t *kl = kept + (size_t)qb * kb;
   const size_t headblk = (size_t)bh * T;
   // padding keys of the last block held by this lane (keys 16t + 4g + r >= nlast)
   int npad_lane = 0;
@@ -904,7 +923,12 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     lsum[u] = 0.f;
     bounded = bounded && (m[u] <= BOUND_LIMIT);
   }
-  if (BOUND) {
+  if constexpr (DUMP) {
+    // every score is read back, whatever the bound decides
+    kept_loop_piped<D, QK8, FINE, true>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr,
+                                        (const uint4 *)vt, headblk, dqi, T, nlast, lane, dmp);
+    return;
+  } else if (BOUND) {
     const bool fail = __ballot(!bounded) != 0ull;
     if (lane == 0) flags[qb] = fail ? 1 : 0;
     if (fail) return;
@@ -1075,34 +1099,6 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   }
 }
 
-// int32 QK^T of (bh, i, j) triples, one wave per triple; same fragment loads
-// and MFMA sequence as k_attn.  Out-of-range triples give zeros.
-template <int D>
-__global__ __launch_bounds__(64) void k_debug_qk(const int8_t *__restrict__ q8,
-                                                 const int8_t *__restrict__ k8, int BH, int T,
-                                                 const int32_t *__restrict__ pairs, int n,
-                                                 int32_t *__restrict__ out) {
-  constexpr int KC = D / 64;
-  const int p = blockIdx.x, lane = threadIdx.x;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int bh = pairs[3 * p], i = pairs[3 * p + 1], j = pairs[3 * p + 2];
-  int32_t *o = out + (size_t)p * BLK * BLK;
-  if (bh < 0 || bh >= BH || i < 0 || i >= T || j < 0 || j >= T) {
-    for (int x = lane; x < BLK * BLK; x += 64) o[x] = 0;
-    return;
-  }
-  v4i qf[4][KC], kf[4][KC], s[4][4];
-  load_q8<D>(q8 + ((size_t)bh * T + i) * BLK * D, qf, lane);
-  load_q8<D>(k8 + ((size_t)bh * T + j) * BLK * D, kf, lane);
-  qk_int8<D>(kf, qf, s);
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[(16 * u + l16) * BLK + 16 * t + 4 * g + r] = s[t][u][r];
-}
-
 template <int D, bool LIN, bool QK8, bool FINE>
 static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *out,
                           hipStream_t st) {
@@ -1110,12 +1106,12 @@ static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, ui
   dim3 grid((nqb + 3) / 4), block(256);
   const float qk_scale = p.sm_scale * LOG2E;
   const void *kfr = QK8 ? (const void *)ws.k8 : (const void *)ws.kbf;
-  hipLaunchKernelGGL((k_attn<D, LIN, true, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
-                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, ws.lse,
-                     ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale);
-  hipLaunchKernelGGL((k_attn<D, LIN, false, QK8, FINE>), grid, block, 0, st, ws.q8, kfr, ws.dq,
-                     ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags, ws.lse,
-                     ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale);
+  hipLaunchKernelGGL((k_attn<D, LIN, true, QK8, FINE, false>), grid, block, 0, st, ws.q8, kfr,
+                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
+                     ws.lse, ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale, nullptr, nullptr, 0);
+  hipLaunchKernelGGL((k_attn<D, LIN, false, QK8, FINE, false>), grid, block, 0, st, ws.q8, kfr,
+                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
+                     ws.lse, ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale, nullptr, nullptr, 0);
 }
 
 template <int D, bool QK8, bool FINE>
@@ -1145,13 +1141,25 @@ void launch_attn(const Plan &p, const uint16_t *q, const WsPtrs &ws, uint16_t *o
     launch_attn_m<64>(p, q, ws, out, st);
 }
 
+template <int D, bool FINE>
+static void launch_debug_qk_t(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n,
+                              int32_t *out, hipStream_t st) {
+  const int nqb = p.BH * p.T;
+  hipLaunchKernelGGL((k_attn<D, false, true, true, FINE, true>), dim3((n + 3) / 4), dim3(256), 0, st,
+                     ws.q8, (const void *)ws.k8, ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept,
+                     nullptr, ws.hi, ws.wsw, nullptr, ws.flags, ws.lse, ws.os, p.N, p.T, p.kb, nqb,
+                     p.F, p.sm_scale * LOG2E, pairs, out, n);
+}
+
 void launch_debug_qk(const Plan &p, const WsPtrs &ws, const int32_t *pairs, int n, int32_t *out,
                      hipStream_t st) {
   if (n <= 0) return;
   if (p.d == 128)
-    hipLaunchKernelGGL(k_debug_qk<128>, dim3(n), dim3(64), 0, st, ws.q8, ws.k8, p.BH, p.T, pairs, n, out);
+    p.qk_fine ? launch_debug_qk_t<128, true>(p, ws, pairs, n, out, st)
+              : launch_debug_qk_t<128, false>(p, ws, pairs, n, out, st);
   else
-    hipLaunchKernelGGL(k_debug_qk<64>, dim3(n), dim3(64), 0, st, ws.q8, ws.k8, p.BH, p.T, pairs, n, out);
+    p.qk_fine ? launch_debug_qk_t<64, true>(p, ws, pairs, n, out, st)
+              : launch_debug_qk_t<64, false>(p, ws, pairs, n, out, st);
 }
 
 }  // namespace sla

@@ -186,9 +186,11 @@ def isa(tmp_path_factory):
     return parse(out)
 
 
-# the d = 128 pipelined (bound-path) instances, mangled: k_attn<128, LIN, true, QK8, FINE>
-HOT = ["_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb0E", "_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb1E",
-       "_ZN3sla6k_attnILi128ELb1ELb1ELb0ELb0E", "_ZN3sla6k_attnILi128ELb0ELb1ELb1ELb0E"]
+# the d = 128 pipelined (bound-path) instances, mangled:
+# k_attn<128, LIN, true, QK8, FINE, DUMP>, including the int32 read-back form
+HOT = ["_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb0ELb0E", "_ZN3sla6k_attnILi128ELb1ELb1ELb1ELb1ELb0E",
+       "_ZN3sla6k_attnILi128ELb1ELb1ELb0ELb0ELb0E", "_ZN3sla6k_attnILi128ELb0ELb1ELb1ELb0ELb0E",
+       "_ZN3sla6k_attnILi128ELb0ELb1ELb1ELb0ELb1E", "_ZN3sla6k_attnILi128ELb0ELb1ELb1ELb1ELb1E"]
 
 
 def test_asm_mfma_results_are_not_read_early(isa):

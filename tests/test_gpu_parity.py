@@ -242,8 +242,12 @@ def test_explicit_sm_scale():
     full_compare(synth.Workload("scale", 1, 1, 777, 128, 0.2, seed=9), sm_scale=0.05)
 
 
-def test_int32_qk_tiles_bit_exact():
-    wl = synth.Workload("qk", 1, 2, 1000, 128, 0.5, seed=2)
+@pytest.mark.parametrize("d", [128, 64])
+def test_int32_qk_tiles_bit_exact(d):
+    """The score accumulators of the attention kernel's own bound-path loop,
+    read back, equal the exact int32 products of the oracle's codes (the last
+    block, 15, is ragged: 40 keys)."""
+    wl = synth.Workload("qk", 1, 2, 1000, d, 0.5, seed=2)
     m, o, dv, (q, k, v, w) = run(wl)
     T = m.plan.info.T
     triples = [(0, 0, 0), (0, 3, 15), (1, 15, 15), (1, 7, 2), (0, 15, 0)]
