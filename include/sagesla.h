@@ -37,7 +37,8 @@
  *  - All device pointers are device memory of the current HIP device; all
  *    tensors are contiguous, 16-byte aligned.  The workspace is owned by the
  *    caller, at least sla_plan_info()'s workspace_bytes and 256-byte aligned;
- *    one workspace may not serve two calls at once.
+ *    one workspace may not serve two calls at once (sla_attention_fwd_noalloc
+ *    takes none: it uses a static one the library holds).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work: no device allocation, no host synchronisation.
  *  - sla_quantize must run before sla_attention_fwd on the same workspace
@@ -63,7 +64,8 @@ typedef enum {
   SLA_EUNSUPPORTED = 2,  /* valid but not built: d not in {64,128}, block != 64, N too large */
   SLA_EWORKSPACE = 3,    /* workspace smaller than sla_plan_info() says */
   SLA_EHIP = 4,          /* a HIP launch failed */
-  SLA_ENOMEM = 5         /* host allocation of the plan failed */
+  SLA_ENOMEM = 5,        /* host allocation of the plan failed */
+  SLA_ETOOLARGE = 6      /* the plan's workspace exceeds SLA_NOALLOC_WS_BYTES */
 } sla_status;
 
 typedef struct {
@@ -108,6 +110,27 @@ sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
 sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
                              const void *w_proj, void *out, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Size of the workspace the library holds for sla_attention_fwd_noalloc, per
+ * GPU: 64 MiB (B*H = 2, N = 16384, d = 128 takes about 49 MiB). */
+#define SLA_NOALLOC_WS_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): sla_quantize
+ * followed by sla_attention_fwd, same arguments and results, on a workspace
+ * the library holds instead of a caller's.  That workspace is a static device
+ * array of SLA_NOALLOC_WS_BYTES on each GPU the call runs on (the current
+ * device; stream must belong to it); its address is looked up on the first
+ * call on the device, so make that call outside graph capture, and the array
+ * is held until the process ends.  No call allocates device or host memory.
+ * A plan whose workspace_bytes exceed SLA_NOALLOC_WS_BYTES gets
+ * SLA_ETOOLARGE; other argument errors as for the two calls; nothing is
+ * launched on an error.  Every call on one GPU uses the same array, which
+ * keeps the last call's contents (a call reads only what it wrote itself), so
+ * calls that overlap on one GPU (other streams, other threads) race: the
+ * caller serialises them. */
+sla_status sla_attention_fwd_noalloc(sla_plan_t plan, const void *q, const void *k, const void *v,
+                                     const void *w_proj, void *out, void *stream);
 
 /* The two stages of sla_attention_fwd, for callers that schedule or time
  * them separately (same arguments, same order on one stream):

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "sla_internal.h"
@@ -63,6 +64,31 @@ static int selection_rows(int d, int T) {
   return (int)r;
 }
 
+// The workspace of sla_attention_fwd_noalloc: one copy per GPU, at that GPU's
+// own address.  In host code `scratch` names a host-side stand-in, never the
+// device memory: only the per-device address from hipGetSymbolAddress is
+// passed on.
+static __device__ __align__(256) unsigned char scratch[SLA_NOALLOC_WS_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch[MAX_DEVICES];  // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up on the first call on that
+// device (with the device current).
+static sla_status scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SLA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SLA_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SLA_OK;
+}
+
 }  // namespace sla
 
 using namespace sla;
@@ -77,6 +103,7 @@ const char *sla_status_string(sla_status s) {
     case SLA_EWORKSPACE: return "workspace too small";
     case SLA_EHIP: return "HIP launch failed";
     case SLA_ENOMEM: return "host allocation failed";
+    case SLA_ETOOLARGE: return "workspace exceeds the library's static workspace";
   }
   return "unknown status";
 }
@@ -263,6 +290,23 @@ sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, cons
   s = sla_prepare_kv(plan, k, v, w_proj, ws, ws_bytes, stream);
   if (s != SLA_OK) return s;
   return sla_attend(plan, q, out, ws, ws_bytes, stream);
+}
+
+sla_status sla_attention_fwd_noalloc(sla_plan_t plan, const void *q, const void *k, const void *v,
+                                     const void *w_proj, void *out, void *stream) {
+  // the checks of sla_quantize and sla_attention_fwd, all before any launch
+  if (!plan || !q || !k || !v || !out) return SLA_EINVAL;
+  const Plan &p = plan->p;
+  if (p.cfg.use_linear && !w_proj) return SLA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SLA_EINVAL;
+  if (w_proj && !aligned(w_proj, 16)) return SLA_EINVAL;
+  if (p.total > SLA_NOALLOC_WS_BYTES) return SLA_ETOOLARGE;
+  void *ws = nullptr;
+  sla_status s = scratch_ptr(&ws);
+  if (s != SLA_OK) return s;
+  s = sla_quantize(plan, q, k, ws, SLA_NOALLOC_WS_BYTES, stream);
+  if (s != SLA_OK) return s;
+  return sla_attention_fwd(plan, q, k, v, w_proj, out, ws, SLA_NOALLOC_WS_BYTES, stream);
 }
 
 sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr, size_t *bytes) {

@@ -13,12 +13,14 @@ from dataclasses import dataclass
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsagesla.so")
 
-SLA_OK, SLA_EINVAL, SLA_EUNSUPPORTED, SLA_EWORKSPACE, SLA_EHIP, SLA_ENOMEM = range(6)
+SLA_OK, SLA_EINVAL, SLA_EUNSUPPORTED, SLA_EWORKSPACE, SLA_EHIP, SLA_ENOMEM, SLA_ETOOLARGE = range(7)
+NOALLOC_WS_BYTES = 64 << 20  # SLA_NOALLOC_WS_BYTES
 WS_REGIONS = ["QBAR", "KSUM", "KBAR", "MU", "MASK", "KEPT", "Q8", "K8", "DQ", "DK", "LSE"]
 
 EXPORTS = ["sla_plan", "sla_plan_destroy", "sla_plan_info", "sla_quantize", "sla_attention_fwd",
            "sla_prepare_kv", "sla_attend", "sla_status_string", "sla_ws_view",
-           "sla_debug_qk_int32", "sla_quant_b128", "sla_w8a8_gemm", "sla_attention_bwd"]
+           "sla_debug_qk_int32", "sla_quant_b128", "sla_w8a8_gemm", "sla_attention_bwd",
+           "sla_attention_fwd_noalloc"]
 
 
 class SlaError(RuntimeError):
@@ -72,6 +74,8 @@ def lib():
         L.sla_w8a8_gemm.restype = ctypes.c_int
         L.sla_attention_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.sla_attention_bwd.restype = ctypes.c_int
+        L.sla_attention_fwd_noalloc.argtypes = [P, P, P, P, P, P, P]
+        L.sla_attention_fwd_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -308,3 +312,24 @@ def w8a8_gemm(xq, sx, wq, sw, out=None, stream=None):
                                M, N, K, ctypes.c_void_p(y.data_ptr()), _stream_handle(stream)),
            "sla_w8a8_gemm")
     return y
+
+
+def attention_fwd_noalloc(plan: Plan, q, k, v, w, out, stream=None):
+    """sla_attention_fwd_noalloc: the forward (quantisation included) on the
+    library's static per-GPU workspace.  q, k, v, out: contiguous bf16
+    [B,H,N,d] device tensors of the plan's shape; w: bf16 [d,d] or None.
+    Allocates nothing."""
+    import torch
+    B, H, N, d = plan.cfg.B, plan.cfg.H, plan.cfg.N, plan.cfg.d
+    for name, x, shape in (("q", q, (B, H, N, d)), ("k", k, (B, H, N, d)), ("v", v, (B, H, N, d)),
+                           ("out", out, (B, H, N, d))) + ((("w", w, (d, d)),) if w is not None else ()):
+        if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+        if tuple(x.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    ptr = lambda x: ctypes.c_void_p(x.data_ptr() if x is not None else 0)
+    _check(lib().sla_attention_fwd_noalloc(plan.handle, ptr(q), ptr(k), ptr(v), ptr(w), ptr(out),
+                                           ctypes.c_void_p(s.cuda_stream)),
+           "sla_attention_fwd_noalloc")
+    return out
