@@ -12,8 +12,10 @@ time), ms per call (mean, and p10 / median / p90 of the per-call times), the
 per-stage times, the roofline of the dominant kernel (the block-sparse
 attention kernel, timed with HIP events on the stream it runs on) against the
 published peaks and against peaks measured on the same GPU after the timed
-region (MFMA-only kernels, a device copy), and the CPU oracle timed on a
-bounded sample of the same workload.
+region (MFMA-only kernels, a device copy), the SHA-256 of each input as
+uploaded, and the CPU oracle timed on the host's cores: a bounded sample of
+the same workload on one pinned core and on all cores (host CPU model and
+core count recorded), plus the small workloads run in full.
 """
 from __future__ import annotations
 
@@ -102,39 +104,149 @@ def spread(ms):
     return [float(np.percentile(ms, 10)), float(np.median(ms)), float(np.percentile(ms, 90))]
 
 
-def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True, fine=False):
-    """The oracle, single threaded, on one head of the workload: the head's
-    whole selection/quantisation and linear states plus n_blocks query blocks;
-    the head time is extrapolated to all T query blocks and reported as
-    dense-equivalent TFLOP/s (heads are independent and cost the same)."""
+def host_cpu():
+    """CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def oracle_threads(nproc):
+    # worker threads of the all-core runs: the host's cores, at most 16 (a
+    # GPU's share of a shared host)
+    return max(1, min(16, nproc))
+
+
+def _oracle_head(wl, b, h, blocks, qk_int8, fine, barrier=None):
+    """The oracle on head (b, h): selection, quantisation and linear states for
+    the whole head, then the query blocks ``blocks`` (all when None).  Inputs
+    are generated before the clock starts.  Returns (prep seconds, block
+    seconds, thread CPU seconds)."""
     import oracle
-    q, k, v = synth.head_inputs(wl, 0, 0)
+    q, k, v = synth.head_inputs(wl, b, h)
     w = synth.proj_weight(wl)
-    T = oracle.nblocks(wl.N)
-    t0 = time.perf_counter()
+    if barrier is not None:
+        barrier.wait()
+    c0, t0 = time.thread_time(), time.perf_counter()
     prep = oracle.head_prep(q, k, float(np.float32(wl.topk)), fine=fine)
     states = oracle.linear_states(k, v) if wl.use_linear else None
     t1 = time.perf_counter()
+    if barrier is not None:
+        barrier.wait()
+        t1 = time.perf_counter()
+    oracle.head_forward(q, k, v, w, float(np.float32(wl.topk)), use_linear=bool(wl.use_linear),
+                        blocks=blocks, prep=prep, states=states, qk_int8=qk_int8, fine=fine)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1, time.thread_time() - c0
+
+
+def _parallel(fn, jobs, threads):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, jobs))
+
+
+def oracle_full(wl, threads, qk_int8=True, fine=False, log_fn=log):
+    """The oracle over the whole workload (every head, every query block) with
+    the (b, h) loop split over ``threads`` threads: wall seconds and the sum
+    of the threads' CPU seconds (the single-core time of the same work)."""
+    t0 = time.perf_counter()
+    heads = wl.heads()
+    r = _parallel(lambda bh: _oracle_head(wl, bh[0], bh[1], None, qk_int8, fine), heads,
+                  min(threads, len(heads)))
+    wall = time.perf_counter() - t0
+    cpu = sum(x[2] for x in r)
+    log_fn(f"[cpu] {wl.name} in full: {wall:.1f}s wall on {min(threads, len(heads))} threads "
+           f"(input generation included), {cpu:.1f} CPU-s")
+    return {"heads": len(heads), "threads": min(threads, len(heads)),
+            "wall_s_incl_input_generation": wall, "cpu_s": cpu,
+            "ms_per_call_single_core": cpu * 1e3}
+
+
+def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True, fine=False, full=("tiny",)):
+    """The oracle on the host's cores, on a bounded sample of the workload.
+
+    Single core: head (0,0) with the process pinned to one core: its whole
+    selection/quantisation and linear states plus n_blocks query blocks, the
+    block time extrapolated to all T blocks.  All cores: the same sample on
+    one head per thread (heads (0,0), (0,1), ...), the selection phase and the
+    block phase each timed by wall clock between barriers; one round of
+    ``threads`` heads is then extrapolated to all B*H heads.  Both reported as
+    dense-equivalent TFLOP/s; the headline value is the all-core one.
+    ``full``: workloads also run in full (all heads and blocks)."""
+    import threading
+    import oracle
+    model, nproc = host_cpu()
+    T = oracle.nblocks(wl.N)
     rng = np.random.default_rng(0)
     blocks = sorted(rng.choice(T, size=min(n_blocks, T), replace=False).tolist())
-    oracle.head_forward(q, k, v, w, float(np.float32(wl.topk)), use_linear=bool(wl.use_linear),
-                        blocks=blocks, prep=prep, states=states, qk_int8=qk_int8)
-    t2 = time.perf_counter()
-    head_s = (t1 - t0) + (t2 - t1) * T / len(blocks)
-    dense = 4.0 * wl.N * wl.N * wl.d
-    log_fn(f"[cpu] prep+states {t1 - t0:.2f}s, {len(blocks)} blocks {t2 - t1:.2f}s, "
+    dense = 4.0 * wl.B * wl.H * wl.N * wl.N * wl.d
+    BH = wl.B * wl.H
+
+    # single core, pinned
+    prev = os.sched_getaffinity(0)
+    core = min(prev)
+    os.sched_setaffinity(0, {core})
+    try:
+        tp, tb, _ = _oracle_head(wl, 0, 0, blocks, qk_int8, fine)
+    finally:
+        os.sched_setaffinity(0, prev)
+    head_s = tp + tb * T / len(blocks)
+    log_fn(f"[cpu] one core: prep+states {tp:.2f}s, {len(blocks)} blocks {tb:.2f}s, "
            f"head extrapolated {head_s:.1f}s")
-    return {
-        "value": dense / head_s / 1e12,
+
+    # all cores
+    threads = min(oracle_threads(nproc), BH)
+    bar = threading.Barrier(threads)
+    heads = wl.heads()[:threads]
+    t0 = time.perf_counter()
+    r = _parallel(lambda bh: _oracle_head(wl, bh[0], bh[1], blocks, qk_int8, fine, bar), heads,
+                  threads)
+    wall_prep = max(x[0] for x in r)
+    wall_blocks = max(x[1] for x in r)
+    round_s = wall_prep + wall_blocks * T / len(blocks)
+    job_s = round_s * -(-BH // threads)
+    log_fn(f"[cpu] {threads} threads: prep+states {wall_prep:.2f}s, {len(blocks)} blocks "
+           f"{wall_blocks:.2f}s wall (total {time.perf_counter() - t0:.1f}s), "
+           f"call extrapolated {job_s:.0f}s")
+
+    res = {
+        "value": dense / job_s / 1e12,
         "unit": "TFLOP/s (dense-equivalent)",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"head (0,0) of {wl.name}: selection, quantisation and linear states for "
-                   f"the whole head ({t1 - t0:.1f}s) plus {len(blocks)} of {T} query blocks "
-                   f"({t2 - t1:.1f}s), extrapolated to the head ({head_s:.0f}s); "
-                   f"single thread, {platform.processor() or platform.machine()}"),
-        "ms_per_call_extrapolated": head_s * wl.B * wl.H * 1e3,
+        "sample": (f"{wl.name}: per head, selection, quantisation and linear states for the "
+                   f"whole head plus {len(blocks)} of {T} query blocks (the same blocks on "
+                   f"every head), block time extrapolated to the head; all cores: heads "
+                   f"(0,0)..(0,{threads - 1}) on {threads} threads, one round extrapolated to "
+                   f"{BH} heads ({-(-BH // threads)} rounds); one core: head (0,0) pinned to "
+                   f"core {core}"),
+        "host_cpu": model,
+        "nproc": nproc,
+        "ms_per_call_extrapolated": job_s * 1e3,
+        "all_core": {"threads": threads, "prep_wall_s": wall_prep,
+                     "blocks_wall_s": wall_blocks, "ms_per_call_extrapolated": job_s * 1e3},
+        "single_core": {"value": dense / (head_s * BH) / 1e12, "core": core, "prep_s": tp,
+                        "blocks_s": tb, "head_s_extrapolated": head_s,
+                        "ms_per_call_extrapolated": head_s * BH * 1e3},
     }
+    if full:
+        res["full_runs"] = {name: oracle_full(synth.WORKLOADS[name], oracle_threads(nproc),
+                                              qk_int8, fine, log_fn)
+                            for name in full}
+    return res
+
+
+def input_sha256(**arrays):
+    """SHA-256 of each input's bytes as generated on the host (bf16 bits,
+    row-major), the form they are uploaded in."""
+    return {k: hashlib.sha256(np.ascontiguousarray(a).data).hexdigest() for k, a in arrays.items()}
 
 
 def bench_w8a8(args, dev):
@@ -317,8 +429,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan14b-720p", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--cpu-blocks", type=int, default=360,
-                    help="query blocks the CPU oracle baseline computes (0 = skip)")
+    ap.add_argument("--cpu-blocks", type=int, default=240,
+                    help="query blocks per head the CPU oracle baseline computes (0 = skip)")
+    ap.add_argument("--cpu-full", default="tiny,wan1.3b-480p",
+                    help="workloads the CPU oracle also runs in full on all cores "
+                         "(comma-separated; empty = none)")
     ap.add_argument("--qk", choices=("int8", "int8-fine", "bf16"), default="int8",
                     help="QK^T operands: int8 (SageSLA with one scale per 64-row block, the "
                          "default), int8-fine (one Q scale per 16 rows, one K scale per 4 "
@@ -372,6 +487,7 @@ def main():
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     Q, K, V, W = up(q), up(k), up(v), up(w)
+    sha = input_sha256(q=q, k=k, v=v, w=w)
     del q, k, v
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
     qk_int8 = args.qk != "bf16"
@@ -464,10 +580,13 @@ def main():
             "frac_of_measured": mp and achieved / blended_measured,
         },
         "measured_peaks": mp,
+        "inputs_sha256": sha,
     }
     if args.cpu_blocks > 0:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks, qk_int8=qk_int8, fine=fine)
+        full = tuple(x for x in args.cpu_full.split(",") if x)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_blocks, qk_int8=qk_int8, fine=fine,
+                                           full=full)
     print(json.dumps(res), flush=True)
 
 

@@ -67,3 +67,26 @@ def test_traffic_entry_is_null_or_positive():
         assert t == meta["bytes_per_launch"]
     else:
         assert t is None
+
+
+def test_cpu_baseline_fields_on_the_tiny_workload():
+    b = load_bench()
+    wl = synth.WORKLOADS["tiny"]
+    r = b.cpu_baseline(wl, 8, log_fn=lambda *a: None, full=("tiny",))
+    model, nproc = b.host_cpu()
+    assert r["kind"] == "oracle" and r["host_cpu"] == model and r["nproc"] == nproc >= 1
+    assert r["cores"] == r["all_core"]["threads"] == min(b.oracle_threads(nproc), wl.B * wl.H)
+    assert r["value"] > 0 and r["single_core"]["value"] > 0
+    assert r["full_runs"]["tiny"]["heads"] == wl.B * wl.H
+    # the process affinity is restored after the pinned single-core run
+    assert len(os.sched_getaffinity(0)) == nproc
+
+
+def test_input_sha256_is_of_the_uploaded_bytes():
+    import hashlib
+    import numpy as np
+    b = load_bench()
+    a = np.arange(6, dtype=np.uint16).reshape(2, 3)
+    assert b.input_sha256(q=a)["q"] == hashlib.sha256(a.tobytes()).hexdigest()
+    # e3b0c442...: SHA-256 of the empty string (FIPS 180-4 test vector)
+    assert b.input_sha256(e=np.zeros(0, np.uint16))["e"].startswith("e3b0c44298fc1c14")
