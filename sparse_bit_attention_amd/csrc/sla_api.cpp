@@ -39,6 +39,7 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.wsw = (uint16_t *)(b + p.off[R_WSW]);
   w.hb = (uint16_t *)(b + p.off[R_HB]);
   w.hi = (uint16_t *)(b + p.off[R_HI]);
+  w.sc = (float *)(b + p.off[R_SC]);
   w.lse = (float *)(b + p.off[R_LSE]);
   w.mt = (uint64_t *)(b + p.off[R_MT]);
   w.mtt = (uint64_t *)(b + p.off[R_MTT]);
@@ -52,16 +53,6 @@ WsPtrs ws_ptrs(const Plan &p, void *ws) {
   w.dkl = (float *)(b + p.off[R_DKL]);
   w.dvl = (float *)(b + p.off[R_DVL]);
   return w;
-}
-
-// Rows of query blocks per selection workgroup: R*(d + T) floats plus 1 KiB
-// of per-wave scratch must fit in 64 KiB of LDS; a multiple of 4 (one row per
-// wave) when possible.
-static int selection_rows(int d, int T) {
-  long r = ((64L * 1024 - 1024) / 4) / (long)(d + T);
-  if (r > 16) r = 16;
-  if (r >= 4) r &= ~3L;
-  return (int)r;
 }
 
 // The workspace of sla_attention_fwd_noalloc: one copy per GPU, at that GPU's
@@ -124,8 +115,9 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   if (c.d != 64 && c.d != 128) return SLA_EUNSUPPORTED;
   const long long T = ((long long)c.N + BLK - 1) / BLK;
   const long long BH = (long long)c.B * c.H;
-  if (sla::selection_rows(c.d, (int)(T > (1 << 30) ? (1 << 30) : T)) < 1) return SLA_EUNSUPPORTED;
   if (BH * T >= (1LL << 31) / BLK) return SLA_EUNSUPPORTED;
+  // the score kernel's grid: one workgroup per (head, 32 query blocks, 256 key blocks)
+  if (BH * ((T + 31) / 32) * ((T + 255) / 256) >= (1LL << 31)) return SLA_EUNSUPPORTED;
 
   sla_plan_s *h = new (std::nothrow) sla_plan_s;
   if (!h) return SLA_ENOMEM;
@@ -150,7 +142,6 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   }
   p.W64 = (p.T + 63) / 64;
   p.F = ((c.d * c.d + c.d) + 127) / 128 * 128;
-  p.rows_sel = selection_rows(c.d, p.T);
   p.lin_on = (c.use_linear == 1 && p.kb < p.T) ? 1 : 0;
   p.qk_int8 = c.qk_int8;
   p.qk_fine = c.qk_fine;
@@ -179,6 +170,7 @@ sla_status sla_plan(const sla_config *cfg, sla_plan_t *out) {
   p.size[R_WSW] = p.lin_on ? (size_t)p.d * p.d * 2 : 0;
   p.size[R_HB] = p.lin_on ? bt * p.F * 2 : 0;
   p.size[R_HI] = p.lin_on ? bt * p.F * 2 : 0;
+  p.size[R_SC] = bt * p.T * 4;
   p.size[R_LSE] = bt * BLK * 4;
   p.size[R_MT] = p.bwd ? bt * p.W64 * 8 : 0;
   p.size[R_MTT] = p.bwd && p.lin_on ? bt * p.W64 * 8 : 0;

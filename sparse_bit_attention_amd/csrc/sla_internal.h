@@ -32,6 +32,7 @@ enum Region {
   R_WSW,  // bf16 projection in wfrag_off order                  [d*d]
   R_HB,   // bf16 per key block linear state (hstate_off order)  [BH][T][F]
   R_HI,   // bf16 per query block marginal state (same order)    [BH][T][F]
+  R_SC,   // f32 block scores, row i over key blocks j           [BH][T][T]
   // backward pass (plans with backward = 1)
   R_MT,   // u64 transposed mask, row j = key block, bits = query blocks [BH][T][W64]
   R_MTT,  // u64 the same, word-major (marginal GEMM operand)    [BH][W64][T]
@@ -51,7 +52,6 @@ struct Plan {
   sla_config cfg;
   int B, H, N, d, BH, T, kb, W64;
   int F;          // per-block linear-state length, d*d + d padded to 128
-  int rows_sel;   // query-block rows per selection workgroup
   int lin_on;     // linear branch present (use_linear and kb < T)
   int qk_int8;
   int qk_fine;    // finer INT8 scales: 16 query rows, 4 keys per scale
@@ -69,6 +69,7 @@ struct WsPtrs {
   int32_t *kept, *flags;
   int8_t *q8, *k8;
   uint16_t *vt, *kbf, *wsw, *hb, *hi;
+  float *sc;
 };
 
 WsPtrs ws_ptrs(const Plan &p, void *ws);

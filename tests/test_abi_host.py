@@ -76,7 +76,8 @@ def plan_status(**kw):
     ({"topk": 0.0}, sla.SLA_OK),
     ({"topk": 1.0}, sla.SLA_OK),
     ({"N": 1}, sla.SLA_OK),
-    ({"N": 2_000_000}, sla.SLA_EUNSUPPORTED),
+    ({"N": 2_000_000}, sla.SLA_OK),
+    ({"N": 2_000_000_000}, sla.SLA_EUNSUPPORTED),
     ({"qk_int8": 0}, sla.SLA_OK),
     ({"qk_int8": 0, "d": 128}, sla.SLA_OK),
     ({"qk_int8": 2}, sla.SLA_EINVAL),

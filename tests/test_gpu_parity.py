@@ -355,6 +355,37 @@ def test_full_size_sampled_parity(name):
     assert_close(np.concatenate(G), np.concatenate(R), name)
 
 
+def test_long_sequence_selection():
+    """T = 2188 key blocks, more than the 2048 whose keys a selection wave
+    holds in registers (the selection then re-reads them each pass): masks,
+    kept lists, means and codes bit-exact on the head, outputs at the bar on
+    sampled blocks (ragged last block: 32 rows)."""
+    wl = synth.Workload("long", 1, 1, 140000, 64, 0.02, seed=41)
+    inputs = synth.all_inputs(wl)
+    m, o, dv, _ = run(wl, inputs=inputs)
+    assert m.plan.info.T == 2188
+    mask_properties(m)
+    q, k, v, w = inputs
+    T = m.plan.info.T
+    prep = check_head_prep(m, wl, 0, 0, q[0, 0], k[0, 0])
+    got, ref = compare_blocks(host_u16(o)[0, 0], wl, q[0, 0], k[0, 0], v[0, 0], w, prep,
+                              sorted({0, 1, T // 2, T - 1}))
+    assert_close(got, ref, wl.name)
+
+
+@pytest.mark.parametrize("N", [44000, 64000, 96000, 108800, 128000])
+def test_selection_register_buckets(N):
+    """Selection holds ceil(T/64) keys per lane in 12, 16, 24, 28 or 32
+    registers (T = 688, 1000, 1500, 1700, 2000): masks, kept lists, means and
+    codes of the head bit-exact."""
+    wl = synth.Workload(f"sel{N}", 1, 1, N, 64, 0.07, use_linear=0, seed=N % 997)
+    inputs = synth.all_inputs(wl)
+    m, o, dv, _ = run(wl, inputs=inputs)
+    mask_properties(m)
+    q, k, v, w = inputs
+    check_head_prep(m, wl, 0, 0, q[0, 0], k[0, 0])
+
+
 def test_dense_outlier_against_float64_dense_attention():
     """The dense INT8 stress workload (topk 1, no linear branch, K offsets
     ~N(0,16) with one channel x20) at full size against float64 dense softmax
