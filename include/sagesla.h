@@ -95,16 +95,18 @@ sla_status sla_plan_destroy(sla_plan_t plan);
  * workspace_bytes = workspace size needed.  Any output pointer may be NULL. */
 sla_status sla_plan_info(sla_plan_t plan, int32_t *T, int32_t *kb, size_t *workspace_bytes);
 
-/* Selection and quantisation (steps 1-6): block pooling, K mean, block
- * scores, top-k mask and kept lists, INT8 Q and K' with their scales, all into
- * the workspace (plain SLA: a bf16 copy of K instead of the INT8 step).
+/* Selection and Q quantisation (steps 1-5): block pooling, K mean, block
+ * scores, top-k mask and kept lists, INT8 Q with its scales, all into the
+ * workspace (plain SLA: no INT8 step).  Step 6, K' to INT8, runs in
+ * sla_prepare_kv, which reads K once for it and for the linear states.
  * q, k: bf16 [B,H,N,d]. */
 sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
                         size_t ws_bytes, void *stream);
 
-/* Attention (steps 7-9): V re-layout and per-key-block linear states,
- * marginal-block states per query block, block-sparse INT8/bf16 flash
- * attention with the linear branch and projection fused in its epilogue.
+/* Attention (steps 6-9): K' INT8 codes and scales (plain SLA: a bf16 copy of
+ * K), V re-layout and per-key-block linear states, marginal-block states per
+ * query block, block-sparse INT8/bf16 flash attention with the linear branch
+ * and projection fused in its epilogue.
  * w_proj: bf16 [d][d] ([d_out][d_in]); may be NULL when use_linear is 0.
  * out: bf16 [B,H,N,d]; padding rows are never written. */
 sla_status sla_attention_fwd(sla_plan_t plan, const void *q, const void *k, const void *v,
@@ -134,8 +136,9 @@ sla_status sla_attention_fwd_noalloc(sla_plan_t plan, const void *q, const void 
 
 /* The two stages of sla_attention_fwd, for callers that schedule or time
  * them separately (same arguments, same order on one stream):
- * sla_prepare_kv: V re-layout, per key block linear states and the marginal
- *   states per query block (the last two only when the linear branch is on);
+ * sla_prepare_kv: K' INT8 codes and scales (plain SLA: the bf16 K copy), V
+ *   re-layout, per key block linear states and the marginal states per query
+ *   block (the last two only when the linear branch is on);
  * sla_attend: the block-sparse attention kernel with the linear branch and
  *   projection in its epilogue, writing out.
  * Needs sla_quantize first; sla_attend needs sla_prepare_kv first. */
@@ -201,7 +204,8 @@ sla_status sla_ws_view(sla_plan_t plan, void *ws, int32_t which, void **dev_ptr,
  * range).  Runs the attention kernel's own bound-path loop, with kept list
  * {j} for query block (bh, i), and stores each score accumulator (minus the
  * loop's bias) where the softmax reads it; nothing else is written.  Needs
- * sla_quantize first and qk_int8 = 1; n >= 0 (else SLA_EINVAL). */
+ * sla_quantize and sla_prepare_kv first (Q8 and K8) and qk_int8 = 1; n >= 0
+ * (else SLA_EINVAL). */
 sla_status sla_debug_qk_int32(sla_plan_t plan, const void *ws, const int32_t *dev_pairs, int32_t n,
                               int32_t *dev_out, void *stream);
 

@@ -18,23 +18,38 @@
 
 namespace sla {
 
-// One workgroup (4 waves) per key block.  LDS: V and phi(K) as row-major bf16
+// One workgroup (4 waves) per key block.  KQ = 1 or 2: the block's K' = K - mu
+// is also quantised to INT8 here (K is read once for both): one scale per
+// block (KQ = 1) or per 4 keys (KQ = 2, the finer SageAttention2++-style
+// granularity); k' = float32(K - mu[c]), scale = amax / 127 over the group's
+// valid rows, codes = rint(k' * float32(127 / amax)) clamped to [-127, 127]
+// (0 for padding rows) in the i8_off fragment order; dkn = the largest
+// scale * ||k8 row|| (times 1 + 2^-20) over the block's groups, dkx = the
+// largest scale.  LDS: V and phi(K) as row-major bf16
 // [key][channel] tiles; the pitch (D + 16 elements) keeps the rows 8-byte
 // aligned and puts four consecutive rows on distinct banks, so operand
 // fragments come straight from the transposing read.  The state is computed
 // as H = phi(K)^T V (rows: phi channel c, columns: value channel c2), whose
 // accumulators hold four consecutive c per lane: one 8-byte store each into
 // the hstate_off order.
-template <int D, bool LIN>
+template <int D, bool LIN, int KQ>
 __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
-                                                 const uint16_t *__restrict__ V, int N, int T,
+                                                 const uint16_t *__restrict__ V,
+                                                 const float *__restrict__ mu, int N, int T,
                                                  int F, uint16_t *__restrict__ vt,
-                                                 uint16_t *__restrict__ hb) {
+                                                 uint16_t *__restrict__ hb,
+                                                 int8_t *__restrict__ k8, float *__restrict__ dk,
+                                                 float *__restrict__ dkn,
+                                                 float *__restrict__ dkx) {
   constexpr int P = D + 16;  // row pitch in bf16
   constexpr int CG = D / 16;
   constexpr int KC32 = D / 32;
   constexpr int MT = CG / 4;  // row tiles (16 phi channels) per wave
+  constexpr int NG = KQ == 2 ? 16 : 1;  // K' scale groups per block
+  constexpr bool LOADK = LIN || KQ > 0;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 64 * P];
+  __shared__ __attribute__((aligned(16))) int8_t s8[KQ > 0 ? 64 * D : 16];
+  __shared__ uint32_t s_amax[NG], s_gsq[NG];  // float bits (all values >= 0)
   uint16_t *sv = smem, *sk = smem + 64 * P;
   const int blk = blockIdx.x;
   const int bh = blk / T, j = blk - bh * T;
@@ -42,6 +57,7 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const size_t base = ((size_t)bh * N + (size_t)j * BLK) * D;
+  if (KQ > 0 && tid < NG) s_amax[tid] = s_gsq[tid] = 0u;  // visible after the staging barrier
 
   // stage V and K rows (zeros past the valid rows); all loads are issued
   // before any is used
@@ -53,7 +69,7 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
     const int r = x / (D / 4), c = (x - r * (D / 4)) * 4;
     const int rc = r < n ? r : n - 1;  // a valid row; zeroed below
     vv[e] = *(const uint2 *)(V + base + (size_t)rc * D + c);
-    if (LIN) kk[e] = *(const uint2 *)(K + base + (size_t)rc * D + c);
+    if (LOADK) kk[e] = *(const uint2 *)(K + base + (size_t)rc * D + c);
   }
 #pragma unroll
   for (int e = 0; e < NX; ++e) {
@@ -64,6 +80,29 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
     if (LIN) *(uint2 *)(sk + r * P + c) = ok ? kk[e] : make_uint2(0u, 0u);
   }
   __syncthreads();
+
+  // K' quantisation, first half: each thread holds channels c .. c+3 of rows
+  // tid / (D/4) + (256 / (D/4)) e; for every e the wave's 64 lanes lie in one
+  // scale group, so a wave max then one LDS max per (wave, e) gives each
+  // group's amax (exact in any order)
+  constexpr int RPE = 256 / (D / 4);  // rows per piece index e
+  const int kc0 = (tid % (D / 4)) * 4;
+  float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (KQ > 0) {
+    m4 = *(const float4 *)(mu + (size_t)bh * D + kc0);
+#pragma unroll
+    for (int e = 0; e < NX; ++e) {
+      const int r = tid / (D / 4) + RPE * e;
+      const uint2 v = kk[e];
+      float a = fmaxf(fmaxf(fabsf(bf2f(v.x & 0xFFFF) - m4.x), fabsf(bf2f(v.x >> 16) - m4.y)),
+                      fmaxf(fabsf(bf2f(v.y & 0xFFFF) - m4.z), fabsf(bf2f(v.y >> 16) - m4.w)));
+      if (r >= n) a = 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      const int q = NG == 1 ? 0 : (RPE * e + 64 * w / (D / 4)) / 4;
+      if (lane == 0) atomicMax(&s_amax[q], __float_as_uint(a));
+    }
+  }
 
   // phi(K) rows in float32, rounded to bf16 in place; four threads per row
   // (D/4 channels each, max and sum combined by shuffles); padding rows
@@ -98,6 +137,59 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
       *(uint32_t *)(row + c) = pack2bf(x[c] * inv, x[c + 1] * inv);
   }
   __syncthreads();
+
+  // K' quantisation, second half: codes into LDS in fragment order, each
+  // row's squared code norm (a sum over the row's D/4 lanes), its group max
+  if constexpr (KQ > 0) {
+    constexpr int KC = D / 64;
+#pragma unroll
+    for (int e = 0; e < NX; ++e) {
+      const int r = tid / (D / 4) + RPE * e;
+      const int q = NG == 1 ? 0 : (RPE * e + 64 * w / (D / 4)) / 4;
+      const float amax = __uint_as_float(s_amax[q]);
+      const float inv = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
+      const uint2 v = kk[e];
+      const float xs[4] = {bf2f(v.x & 0xFFFF) - m4.x, bf2f(v.x >> 16) - m4.y,
+                           bf2f(v.y & 0xFFFF) - m4.z, bf2f(v.y >> 16) - m4.w};
+      uint32_t packed = 0;
+      int sq = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        float y = __builtin_rintf(xs[x] * inv);
+        y = fminf(fmaxf(y, -127.f), 127.f);
+        const int code = (int)y;
+        sq += code * code;
+        packed |= ((uint32_t)(uint8_t)(int8_t)code) << (8 * x);
+      }
+      if (r >= n) packed = 0, sq = 0;
+      *(uint32_t *)(&s8[i8_off(r, kc0, KC)]) = packed;
+#pragma unroll
+      for (int off = D / 8; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+      float gm = (float)sq;
+#pragma unroll
+      for (int off = D / 4; off < 64; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off, 64));
+      if (lane == 0) atomicMax(&s_gsq[q], __float_as_uint(gm));
+    }
+    __syncthreads();
+    {
+      const uint4 *src = (const uint4 *)s8;
+      uint4 *dst = (uint4 *)(k8 + (size_t)blk * BLK * D);
+#pragma unroll
+      for (int it = 0; it < (BLK * D) / (16 * 256); ++it) dst[it * 256 + tid] = src[it * 256 + tid];
+    }
+    if (tid < NG) dk[(size_t)blk * NG + tid] = (float)((double)__uint_as_float(s_amax[tid]) / 127.0);
+    if (tid == 0) {
+      float bmax = 0.f, dmax = 0.f;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        const float delta = (float)((double)__uint_as_float(s_amax[q]) / 127.0);
+        bmax = fmaxf(bmax, delta * (sqrtf(__uint_as_float(s_gsq[q])) * (1.0f + 0x1p-20f)));
+        dmax = fmaxf(dmax, delta);
+      }
+      dkn[blk] = bmax;
+      dkx[blk] = dmax;
+    }
+  }
 
   // V fragments (value channels 16 bt .., keys 32 kc2 ..) in the kmaj order
   // the attention kernel reads: B operands here, written out as they are;
@@ -417,17 +509,28 @@ __global__ __launch_bounds__(512, 1) void k_marginal(const uint64_t *__restrict_
 void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const WsPtrs &ws,
                     hipStream_t st) {
   dim3 grid(p.BH * p.T), block(256);
-  if (p.d == 128) {
-    if (p.lin_on)
-      hipLaunchKernelGGL((k_kv_prep<128, true>), grid, block, 0, st, k, v, p.N, p.T, p.F, ws.vt, ws.hb);
-    else
-      hipLaunchKernelGGL((k_kv_prep<128, false>), grid, block, 0, st, k, v, p.N, p.T, p.F, ws.vt, ws.hb);
-  } else {
-    if (p.lin_on)
-      hipLaunchKernelGGL((k_kv_prep<64, true>), grid, block, 0, st, k, v, p.N, p.T, p.F, ws.vt, ws.hb);
-    else
-      hipLaunchKernelGGL((k_kv_prep<64, false>), grid, block, 0, st, k, v, p.N, p.T, p.F, ws.vt, ws.hb);
-  }
+#define SLA_KVP(D, LIN, KQ)                                                                   \
+  hipLaunchKernelGGL((k_kv_prep<D, LIN, KQ>), grid, block, 0, st, k, v, ws.mu, p.N, p.T, p.F, \
+                     ws.vt, ws.hb, ws.k8, ws.dk, ws.dkn, ws.dkx)
+#define SLA_KVP_D(D)                                          \
+  do {                                                        \
+    const int kq = p.qk_int8 ? (p.qk_fine ? 2 : 1) : 0;       \
+    if (p.lin_on) {                                           \
+      if (kq == 2) SLA_KVP(D, true, 2);                       \
+      else if (kq == 1) SLA_KVP(D, true, 1);                  \
+      else SLA_KVP(D, true, 0);                               \
+    } else {                                                  \
+      if (kq == 2) SLA_KVP(D, false, 2);                      \
+      else if (kq == 1) SLA_KVP(D, false, 1);                 \
+      else SLA_KVP(D, false, 0);                              \
+    }                                                         \
+  } while (0)
+  if (p.d == 128)
+    SLA_KVP_D(128);
+  else
+    SLA_KVP_D(64);
+#undef SLA_KVP_D
+#undef SLA_KVP
 }
 
 void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st) {

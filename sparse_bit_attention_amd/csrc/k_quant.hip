@@ -144,118 +144,6 @@ __global__ void k_kmean(const float *__restrict__ ksum, int N, int T, int D, flo
   mu[(size_t)bh * D + c] = (float)((double)s / (double)N);
 }
 
-// One wave per (head, block): k' = float32(K - mu[c]); amax over the valid rows
-// of the block, or (FINE) of each group of 4 rows (keys), one scale each;
-// codes = rint(k' * float32(127/amax)) clamped to [-127, 127].  dkn = the
-// largest dk_g * ||k8_s|| over the block's groups and rows (with ||q8_r|| it
-// bounds every int32 score); dkx = the largest dk_g.
-template <int D, bool FINE>
-__global__ __launch_bounds__(256) void k_quant_k(const uint16_t *__restrict__ K,
-                                                 const float *__restrict__ mu, int N, int T,
-                                                 int nblk, int8_t *__restrict__ k8,
-                                                 float *__restrict__ dk, float *__restrict__ dkn,
-                                                 float *__restrict__ dkx) {
-  constexpr int LPR = D / 4;       // lanes per row
-  constexpr int RPI = 64 / LPR;    // rows per step
-  constexpr int STEPS = BLK / RPI;
-  constexpr int KC = D / 64;
-  constexpr int NG = FINE ? 16 : 1;       // scale groups per block
-  constexpr int GS = STEPS / NG;          // steps per group
-  static_assert(GS >= 1 && STEPS % NG == 0, "a scale group is whole steps");
-  __shared__ __attribute__((aligned(16))) int8_t stage[4][64 * D];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int blk = blockIdx.x * 4 + w;
-  const bool live = blk < nblk;
-  const int bh = live ? blk / T : 0, t = live ? blk - (blk / T) * T : 0;
-  const int n = min(BLK, N - t * BLK);
-  const int c0 = 4 * (l % LPR), r0 = l / LPR;
-  const float4 m4 = *(const float4 *)(mu + (size_t)bh * D + c0);
-  const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + c0;
-
-  float xs[STEPS][4];
-  float as[STEPS];
-  uint2 raw[STEPS];
-  if (n == BLK) {
-    // full block: unconditional loads, all in flight at once
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) raw[s] = *(const uint2 *)(K + base + (size_t)(s * RPI + r0) * D);
-  } else {
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      const int r = s * RPI + r0;
-      raw[s] = make_uint2(0u, 0u);
-      if (live && r < n) raw[s] = *(const uint2 *)(K + base + (size_t)r * D);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int r = s * RPI + r0;
-    const uint2 v = raw[s];
-    const bool ok = live && r < n;
-    xs[s][0] = bf2f(v.x & 0xFFFF) - m4.x;
-    xs[s][1] = bf2f(v.x >> 16) - m4.y;
-    xs[s][2] = bf2f(v.y & 0xFFFF) - m4.z;
-    xs[s][3] = bf2f(v.y >> 16) - m4.w;
-    as[s] = ok ? fmaxf(fmaxf(fabsf(xs[s][0]), fabsf(xs[s][1])), fmaxf(fabsf(xs[s][2]), fabsf(xs[s][3])))
-               : 0.f;
-  }
-  // per group: amax over its steps and all lanes (exact in any order)
-  float inv[NG], delta[NG];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    float amax = 0.f;
-#pragma unroll
-    for (int s = q * GS; s < (q + 1) * GS; ++s) amax = fmaxf(amax, as[s]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    delta[q] = (float)((double)amax / 127.0);
-    inv[q] = amax > 0.f ? (float)(127.0 / (double)amax) : 0.f;
-    if (live && l == 0) dk[(size_t)blk * NG + q] = delta[q];
-  }
-  float bmax = 0.f, dmax = 0.f;  // the block's largest dk_g ||k8_s|| and dk_g
-  float gmax = 0.f;              // within the current group: max row ||k8_s||^2
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int r = s * RPI + r0;
-    const int q = s / GS;
-    uint32_t packed = 0;
-    int sq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float y = __builtin_rintf(xs[s][e] * inv[q]);
-      y = fminf(fmaxf(y, -127.f), 127.f);
-      const int code = (int)y;
-      sq += code * code;
-      packed |= ((uint32_t)(uint8_t)(int8_t)code) << (8 * e);
-    }
-    if (r >= n) packed = 0, sq = 0;
-    *(uint32_t *)(&stage[w][i8_off(r, c0, KC)]) = packed;
-    // sum over the LPR lanes holding this row
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
-    gmax = fmaxf(gmax, (float)sq);
-    if ((s + 1) % GS == 0) {
-      // the group's other rows sit in the other lanes of the step
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
-      bmax = fmaxf(bmax, delta[q] * (sqrtf(gmax) * (1.0f + 0x1p-20f)));
-      dmax = fmaxf(dmax, delta[q]);
-      gmax = 0.f;
-    }
-  }
-  if (live && l == 0) {
-    dkn[blk] = bmax;
-    dkx[blk] = dmax;
-  }
-  __syncthreads();
-  if (live) {
-    const uint4 *src = (const uint4 *)stage[w];
-    uint4 *dst = (uint4 *)(k8 + (size_t)blk * BLK * D);
-#pragma unroll
-    for (int it = 0; it < (BLK * D) / (16 * 64); ++it) dst[it * 64 + l] = src[it * 64 + l];
-  }
-}
-
 // bf16 QK^T mode: one wave per (head, block): the raw K rows in bfk_off order
 // (an exact copy, padding rows zero); dkn = the largest row L2 norm of the
 // block (with ||q_r|| it bounds every score of the block); dk = 1 (the logit
@@ -335,21 +223,15 @@ void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st) {
   hipLaunchKernelGGL(k_kmean, dim3(p.BH), dim3(p.d), 0, st, ws.ksum, p.N, p.T, p.d, ws.mu);
 }
 
-void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st) {
+void launch_prep_kbf(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st) {
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
-  if (!p.qk_int8) {
-    if (p.d == 128)
-      hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
-                         ws.dkx);
-    else
-      hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
-                         ws.dkx);
-    return;
-  }
-  auto kern = p.d == 128 ? (p.qk_fine ? k_quant_k<128, true> : k_quant_k<128, false>)
-                         : (p.qk_fine ? k_quant_k<64, true> : k_quant_k<64, false>);
-  hipLaunchKernelGGL(kern, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.k8, ws.dk, ws.dkn, ws.dkx);
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
+                       ws.dkx);
+  else
+    hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
+                       ws.dkx);
 }
 
 }  // namespace sla

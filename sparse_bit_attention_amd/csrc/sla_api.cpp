@@ -233,7 +233,6 @@ sla_status sla_quantize(sla_plan_t plan, const void *q, const void *k, void *ws,
   launch_pool_quant_q(p, (const uint16_t *)q, (const uint16_t *)k, w, st);
   launch_kmean(p, w, st);
   launch_select(p, w, st);
-  launch_quant_k(p, (const uint16_t *)k, w, st);
   return launched();
 }
 
@@ -249,6 +248,7 @@ sla_status sla_prepare_kv(sla_plan_t plan, const void *k, const void *v, const v
   (void)hipGetLastError();
   hipStream_t st = (hipStream_t)stream;
   WsPtrs w = ws_ptrs(p, ws);
+  if (!p.qk_int8) launch_prep_kbf(p, (const uint16_t *)k, w, st);
   launch_kv_prep(p, (const uint16_t *)k, (const uint16_t *)v, w, st);
   if (p.lin_on) {
     launch_w_swizzle(p, (const uint16_t *)w_proj, w, st);

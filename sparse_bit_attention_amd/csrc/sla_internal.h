@@ -78,7 +78,9 @@ void launch_pool_quant_q(const Plan &p, const uint16_t *q, const uint16_t *k, co
                          hipStream_t st);
 void launch_kmean(const Plan &p, const WsPtrs &ws, hipStream_t st);
 void launch_select(const Plan &p, const WsPtrs &ws, hipStream_t st);
-void launch_quant_k(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st);
+// bf16 QK^T mode: K copied in bfk_off order with its block norms
+void launch_prep_kbf(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStream_t st);
+// V re-layout, per key block linear states and (INT8 QK^T) the K' codes and scales
 void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const WsPtrs &ws,
                     hipStream_t st);
 void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st);
