@@ -781,7 +781,7 @@ template <int D, bool LIN, bool BOUND, bool QK8, bool FINE, bool DUMP>
 __global__ __launch_bounds__(256, 1) void k_attn(
     const int8_t *__restrict__ q8, const void *__restrict__ kfr, const float *__restrict__ dq,
     const float *__restrict__ dk, const float *__restrict__ dkn, const float *__restrict__ dkx,
-    const uint16_t *__restrict__ vt,
+    const float *__restrict__ mu, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ kept, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ hi, const uint16_t *__restrict__ wsw, uint16_t *__restrict__ out,
     int32_t *__restrict__ flags, float *__restrict__ lse, uint16_t *__restrict__ os, int N, int T,
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   const int g = lane >> 4, l16 = lane & 15;
   const int nlast = N - (T - 1) * BLK;
 
-  // bf16: the largest key norm over the kept list (one entry per lane and a
+  // bf16: the largest centred key norm over the kept list (one entry per lane and a
   // wave max) before the Q fragments are loaded, so they are not live across
   // it; the INT8 paths take it after the scales below
   float kmax_bf = 0.f;
@@ -859,8 +859,10 @@ __global__ __launch_bounds__(256, 1) void k_attn(
 
   // Upper bound of the row's logits (log2 units): |q_r . k_s| <= ||q_r||
   // ||k_s||, so logit <= dq sm_scale log2(e) ||q_r|| max_j max_s (dk_s ||k_s||)
-  // (INT8: codes and scales, dk per block or per key group; bf16: dq = dk = 1,
-  // with a margin for the float32 sums of the products and norms).
+  // (INT8: codes and scales, dk per block or per key group, K centred on
+  // its mean before quantisation; bf16: dq = dk = 1 and ||k_s - mu|| in
+  // place of ||k_s||, which bounds the logit minus c (q_r . mu), with a
+  // margin for the float32 sums of the products and norms).
   // INT8: one kept entry per lane and a wave max (a serial walk of the list
   // waits for two dependent scalar loads per kept block); the bf16 path keeps
   // the walk (with the wave form its register allocation puts an operand
@@ -885,6 +887,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
   }
   const float dqmax = fmaxf(fmaxf(dqi[0], dqi[1]), fmaxf(dqi[2], dqi[3]));
   bool bounded = !QK8 || dqmax * dkmax <= BIAS_C_LIMIT;
+  float qmu[4] = {0.f, 0.f, 0.f, 0.f};  // bf16: q_r . mu per row
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     float qn;
@@ -905,19 +908,34 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       sq += __shfl_xor(sq, 32, 64);
       qn = sqrtf((float)sq) * (1.0f + 0x1p-20f);
     } else {
-      float sq = 0.f;
+      // also q_r . mu: kmax bounds ||k_s - mu|| (mu = the K mean), so m
+      // bounds the row's logits minus c (q_r . mu) on both sides; that
+      // per-row constant joins the exp2 offset below, which leaves the
+      // softmax unchanged and keeps every probability >= 2^(-2m) (K is not
+      // centred in this mode, and its raw norms would put most rows past
+      // the limit)
+      float sq = 0.f, qm = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
+      for (int kc = 0; kc < KC; ++kc) {
+        const float *mk = mu + (size_t)bh * D + 32 * kc + 8 * g;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t wv = qf[u][kc][e];
           const float lo = bf2f((uint16_t)(wv & 0xFFFF)), hi2 = bf2f((uint16_t)(wv >> 16));
           sq = __builtin_fmaf(lo, lo, sq);
           sq = __builtin_fmaf(hi2, hi2, sq);
+          if constexpr (BOUND) {
+            qm = __builtin_fmaf(lo, mk[2 * e], qm);
+            qm = __builtin_fmaf(hi2, mk[2 * e + 1], qm);
+          }
         }
+      }
       sq += __shfl_xor(sq, 16, 64);
       sq += __shfl_xor(sq, 32, 64);
       qn = sqrtf(sq) * (1.0f + 0x1p-12f);
+      qm += __shfl_xor(qm, 16, 64);
+      qm += __shfl_xor(qm, 32, 64);
+      qmu[u] = qm;
     }
     m[u] = dqi[u] * qn * kmax;
     lsum[u] = 0.f;
@@ -932,6 +950,10 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     const bool fail = __ballot(!bounded) != 0ull;
     if (lane == 0) flags[qb] = fail ? 1 : 0;
     if (fail) return;
+    if constexpr (!QK8) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m[u] = __builtin_fmaf(dqi[u], qmu[u], m[u]);
+    }
     kept_loop_piped<D, QK8, FINE>(qf, o, m, lsum, kl, kb, dk, (const uint4 *)kfr,
                                   (const uint4 *)vt, headblk, dqi, T, nlast, lane);
   } else if constexpr (QK8) {
@@ -1107,10 +1129,10 @@ static void launch_attn_t(const Plan &p, const uint16_t *q, const WsPtrs &ws, ui
   const float qk_scale = p.sm_scale * LOG2E;
   const void *kfr = QK8 ? (const void *)ws.k8 : (const void *)ws.kbf;
   hipLaunchKernelGGL((k_attn<D, LIN, true, QK8, FINE, false>), grid, block, 0, st, ws.q8, kfr,
-                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
+                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.mu, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
                      ws.lse, ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale, nullptr, nullptr, 0);
   hipLaunchKernelGGL((k_attn<D, LIN, false, QK8, FINE, false>), grid, block, 0, st, ws.q8, kfr,
-                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
+                     ws.dq, ws.dk, ws.dkn, ws.dkx, ws.mu, ws.vt, ws.kept, q, ws.hi, ws.wsw, out, ws.flags,
                      ws.lse, ws.os, p.N, p.T, p.kb, nqb, p.F, qk_scale, nullptr, nullptr, 0);
 }
 
@@ -1146,7 +1168,7 @@ static void launch_debug_qk_t(const Plan &p, const WsPtrs &ws, const int32_t *pa
                               int32_t *out, hipStream_t st) {
   const int nqb = p.BH * p.T;
   hipLaunchKernelGGL((k_attn<D, false, true, true, FINE, true>), dim3((n + 3) / 4), dim3(256), 0, st,
-                     ws.q8, (const void *)ws.k8, ws.dq, ws.dk, ws.dkn, ws.dkx, ws.vt, ws.kept,
+                     ws.q8, (const void *)ws.k8, ws.dq, ws.dk, ws.dkn, ws.dkx, ws.mu, ws.vt, ws.kept,
                      nullptr, ws.hi, ws.wsw, nullptr, ws.flags, ws.lse, ws.os, p.N, p.T, p.kb, nqb,
                      p.F, p.sm_scale * LOG2E, pairs, out, n);
 }

@@ -145,11 +145,15 @@ __global__ void k_kmean(const float *__restrict__ ksum, int N, int T, int D, flo
 }
 
 // bf16 QK^T mode: one wave per (head, block): the raw K rows in bfk_off order
-// (an exact copy, padding rows zero); dkn = the largest row L2 norm of the
-// block (with ||q_r|| it bounds every score of the block); dk = 1 (the logit
-// scale is sm_scale alone).
+// (an exact copy, padding rows zero); dkn = the largest L2 norm of a row
+// minus the K mean, ||k_s - mu||, over the block's 64 rows (padding rows
+// count as zero rows, norm ||mu||): with ||q_r|| it bounds q_r . k_s - q_r . mu
+// for every key of the block, the offset the attention kernel subtracts (the
+// softmax is unchanged by a per-row constant); dk = 1 (the logit scale is
+// sm_scale alone).
 template <int D>
-__global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K, int N, int T,
+__global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K,
+                                                  const float *__restrict__ mu, int N, int T,
                                                   int nblk, uint16_t *__restrict__ kbf,
                                                   float *__restrict__ dk, float *__restrict__ dkn,
                                                   float *__restrict__ dkx) {
@@ -165,6 +169,7 @@ __global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K
   const int n = min(BLK, N - t * BLK);
   const int c0 = 4 * (l % LPR), r0 = l / LPR;
   const size_t base = ((size_t)bh * N + (size_t)t * BLK) * D + c0;
+  const float4 m4 = *(const float4 *)(mu + (size_t)bh * D + c0);
 
   uint2 raw[STEPS];
   if (n == BLK) {
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(256) void k_prep_kbf(const uint16_t *__restrict__ K
   for (int s = 0; s < STEPS; ++s) {
     const int r = s * RPI + r0;
     const uint32_t p0 = raw[s].x, p1 = raw[s].y;  // zero for padding rows
-    const float e0 = bf2f(p0 & 0xFFFF), e1 = bf2f(p0 >> 16), e2 = bf2f(p1 & 0xFFFF), e3 = bf2f(p1 >> 16);
+    const float e0 = bf2f(p0 & 0xFFFF) - m4.x, e1 = bf2f(p0 >> 16) - m4.y,
+                e2 = bf2f(p1 & 0xFFFF) - m4.z, e3 = bf2f(p1 >> 16) - m4.w;
     float sq = e0 * e0 + e1 * e1 + e2 * e2 + e3 * e3;
     *(uint2 *)(&stage[w][bfk_off(r, c0, KC32)]) = make_uint2(p0, p1);
 #pragma unroll
@@ -227,11 +233,11 @@ void launch_prep_kbf(const Plan &p, const uint16_t *k, const WsPtrs &ws, hipStre
   const int nblk = p.BH * p.T;
   dim3 grid((nblk + 3) / 4), block(256);
   if (p.d == 128)
-    hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
-                       ws.dkx);
+    hipLaunchKernelGGL(k_prep_kbf<128>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.kbf, ws.dk,
+                       ws.dkn, ws.dkx);
   else
-    hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, p.N, p.T, nblk, ws.kbf, ws.dk, ws.dkn,
-                       ws.dkx);
+    hipLaunchKernelGGL(k_prep_kbf<64>, grid, block, 0, st, k, ws.mu, p.N, p.T, nblk, ws.kbf, ws.dk,
+                       ws.dkn, ws.dkx);
 }
 
 }  // namespace sla
