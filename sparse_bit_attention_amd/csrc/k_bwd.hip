@@ -661,6 +661,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
     kf[kc] = v4u{a.x, a.y, b.x, b.y};
     vf[kc] = v4u{c.x, c.y, d.x, d.y};
   }
+  // Complete these loads here: left pending, the compiler's wait before
+  // their first use inside the loop counts against the loads the loop issues
+  // for the next query block, so every iteration would wait for those too.
+#pragma unroll
+  for (int kc = 0; kc < KC32; ++kc) asm volatile("" : "+v"(kf[kc]), "+v"(vf[kc]));
   v4f adk[CG], adv[CG];
 #pragma unroll
   for (int x = 0; x < CG; ++x) adk[x] = adv[x] = v4f{0.f, 0.f, 0.f, 0.f};
