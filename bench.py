@@ -203,7 +203,7 @@ def cpu_baseline(wl, n_blocks, log_fn=log, qk_int8=True, fine=False, full=("tiny
 
     # all cores
     threads = min(oracle_threads(nproc), BH)
-    bar = threading.Barrier(threads)
+    bar = threading.Barrier(threads, timeout=900)  # a failing worker breaks it instead of hanging the rest
     heads = wl.heads()[:threads]
     t0 = time.perf_counter()
     r = _parallel(lambda bh: _oracle_head(wl, bh[0], bh[1], blocks, qk_int8, fine, bar), heads,
