@@ -13,8 +13,10 @@
 //   per SIMD) of 64 x 64; per K block of 128 the exact int32 products come
 //   from v_mfma_i32_16x16x64_i8 and are folded into float32 accumulators with
 //   one fma by the block's scale product sx * sw (float32), blocks in
-//   ascending order.  X and W tiles pass through LDS (double-buffered, 16-byte
-//   pieces XOR-swizzled by row so the fragment reads spread over all banks).
+//   ascending order.  X and W tiles go from global memory straight into a
+//   3-stage LDS ring by the load-to-LDS instruction, two K blocks ahead of
+//   their use (16-byte pieces XOR-swizzled by row so the fragment reads
+//   spread over all banks).
 //
 // On gfx950 the fold costs two vector ALU instructions per output element per
 // K block (convert, fma): as much issue time as the block's MFMAs, so the
@@ -83,6 +85,23 @@ __global__ __launch_bounds__(256) void k_quant_b128(const uint16_t *__restrict__
 }
 
 constexpr int GM_BM = 128, GM_BN = 256, GM_BK = 128;
+constexpr int GM_STAGES = 3;          // LDS ring of K blocks
+
+// load-to-LDS copy: lane l's 16 bytes land at LDS address lds + 16 l (lds
+// wave-uniform)
+__device__ __forceinline__ void w8_copy16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void w8_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// workgroup barrier without __syncthreads' memory fence (its vmcnt(0) would
+// drain the copies in flight); the wave's LDS reads are complete on arrival
+__device__ __forceinline__ void w8_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 constexpr int GM_G = 4;               // row tiles per ordering group
 constexpr int GM_PITCH = GM_BK;       // bytes per LDS row
 // LDS byte offset of the 16 bytes lane l reads for an MFMA operand: row
@@ -99,9 +118,9 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
                                                       const int8_t *__restrict__ wq,
                                                       const float *__restrict__ sw, int M, int N,
                                                       int K, uint16_t *__restrict__ y) {
-  // two stages of [A 128 rows | B 256 rows] x 128 bytes
+  // a ring of stages of [A 128 rows | B 256 rows] x 128 bytes
   constexpr int STG = (GM_BM + GM_BN) * GM_PITCH;  // bytes per stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STG];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GM_STAGES * STG];
   // Tile order: groups of GM_G row tiles; inside a group the row tile runs
   // fastest, so consecutive workgroups (one XCD, xcd_remap) share a W tile
   // and a group's X tiles are reused across all column tiles.
@@ -119,45 +138,30 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
   // one W scale row per wave (clamped: a wave wholly past N stores nothing)
   const int nb = min((n0 + 64 * wc) / WB, (N - 1) / WB);
 
-  // global -> LDS staging: 384 rows x 8 pieces of 16 bytes, 6 per thread;
-  // piece it = 0..5 of this thread is row (it * 512 + tid) / 8 (A rows
-  // first), 16-byte piece tid % 8.  Rows past M / N read the last row
-  // (their products are never stored).  The six pieces sit in named
-  // registers: an indexed array here is moved by the compiler into LDS (or
-  // scratch), which costs a second LDS round trip per piece.
+  // global -> LDS copies: 384 rows x 8 pieces of 16 bytes per K block; copy
+  // it (0..5) of wave w covers rows 64 it + 8 w .. +7 (A rows first), lane l
+  // row 64 it + 8 w + l/8 at LDS piece l%8, which holds global piece
+  // (l%8) ^ (row%8).  Rows past M / N read the last row (their products are
+  // never stored).
   const int pc = tid & 7;
-  const int8_t *sr0, *sr1, *sr2, *sr3, *sr4, *sr5;
-  int lo0, lo1, lo2, lo3, lo4, lo5;  // LDS byte offsets inside a stage
-#define W8_SRC(I)                                                                          \
-  {                                                                                        \
-    const int row = (I * 512 + tid) >> 3;                                                  \
-    sr##I = (row < GM_BM ? xq + (size_t)min(m0 + row, M - 1) * K                           \
-                         : wq + (size_t)min(n0 + row - GM_BM, N - 1) * K) + 16 * pc;       \
-    lo##I = row * GM_PITCH + 16 * (pc ^ (row & 7));                                        \
+  const int8_t *src_[6];
+  uint32_t dst_[6];
+#pragma unroll
+  for (int it = 0; it < 6; ++it) {
+    const int row = 64 * it + 8 * w + (lane >> 3);
+    src_[it] = (row < GM_BM ? xq + (size_t)min(m0 + row, M - 1) * K
+                            : wq + (size_t)min(n0 + row - GM_BM, N - 1) * K) +
+               16 * (pc ^ (row & 7));
+    dst_[it] = (64 * it + 8 * w) * GM_PITCH;
   }
-  W8_SRC(0) W8_SRC(1) W8_SRC(2) W8_SRC(3) W8_SRC(4) W8_SRC(5)
-#undef W8_SRC
-  uint4 g0, g1, g2, g3, g4, g5;
-#define W8_GLOAD(kb_)                                          \
-  {                                                            \
-    const size_t ko = (size_t)(kb_) * GM_BK;                   \
-    g0 = *(const uint4 *)(sr0 + ko);                           \
-    g1 = *(const uint4 *)(sr1 + ko);                           \
-    g2 = *(const uint4 *)(sr2 + ko);                           \
-    g3 = *(const uint4 *)(sr3 + ko);                           \
-    g4 = *(const uint4 *)(sr4 + ko);                           \
-    g5 = *(const uint4 *)(sr5 + ko);                           \
-  }
-#define W8_LSTORE(s_)                                          \
-  {                                                            \
-    uint8_t *st_ = lds + (s_) * STG;                           \
-    *(uint4 *)(st_ + lo0) = g0;                                \
-    *(uint4 *)(st_ + lo1) = g1;                                \
-    *(uint4 *)(st_ + lo2) = g2;                                \
-    *(uint4 *)(st_ + lo3) = g3;                                \
-    *(uint4 *)(st_ + lo4) = g4;                                \
-    *(uint4 *)(st_ + lo5) = g5;                                \
-  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds;
+  auto copy_kb = [&](int kb_) {
+    const size_t ko = (size_t)kb_ * GM_BK;
+    const uint32_t sb = lds0 + (uint32_t)((kb_ % GM_STAGES) * STG);
+#pragma unroll
+    for (int it = 0; it < 6; ++it)
+      w8_copy16(src_[it] + ko, __builtin_amdgcn_readfirstlane(sb + dst_[it]));
+  };
 
   v4f acc[4][4];
 #pragma unroll
@@ -165,12 +169,20 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  W8_GLOAD(0)
-  W8_LSTORE(0)
-  __syncthreads();
+  // K block kb is copied two blocks ahead; before a block's barrier each
+  // wave waits for its copy of the next block, so the stage read next is
+  // complete, and the barrier also frees the stage the next copy overwrites
+  copy_kb(0);
+  if (KB > 1) {
+    copy_kb(1);
+    w8_wait_vm<6>();
+  } else {
+    w8_wait_vm<0>();
+  }
+  w8_barrier();
   for (int kb = 0; kb < KB; ++kb) {
-    const int s = kb & 1;
-    if (kb + 1 < KB) W8_GLOAD(kb + 1)
+    const int s = kb % GM_STAGES;
+    if (kb + 2 < KB) copy_kb(kb + 2);
     // exact int32 block products: lane (row 16 i + l%16, group g) reads
     // bytes 64 kc + 16 g .. +15 of its row
     v4i af[4][2], bf[4][2];
@@ -189,8 +201,8 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
     const float sc = sx[(size_t)mb * KB + kb] * sw[(size_t)nb * KB + kb];
     v4i ia[2];
     // raised wave priority while this wave issues its products and folds:
-    // the other wave of the SIMD does its LDS reads and staging meanwhile
-    // instead of in lockstep (4% faster)
+    // the other wave of the SIMD does its LDS reads meanwhile instead of in
+    // lockstep
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t <= 16; ++t) {
@@ -208,11 +220,9 @@ __global__ __launch_bounds__(512, 1) void k_w8a8_gemm(const int8_t *__restrict__
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (kb + 1 < KB) W8_LSTORE(s ^ 1)
-    __syncthreads();
+    if (kb + 2 < KB) w8_wait_vm<6>(); else w8_wait_vm<0>();
+    w8_barrier();
   }
-#undef W8_GLOAD
-#undef W8_LSTORE
   // store bf16: lane holds rows 4 (l/16) + r of column l%16 of each 16 x 16 tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
