@@ -28,22 +28,24 @@ def dev(a):
     return t.view(torch.bfloat16).cuda()
 
 
-# (workload, qk_fine): a call that fills most of the static workspace, then
-# smaller ones (ragged N, the other head dim, fine scales, no linear branch)
+# (workload, qk mode): a call that fills most of the static workspace, then
+# smaller ones (ragged N, the other head dim, fine scales, no linear branch,
+# plain SLA with bf16 QK^T)
 CALLS = [
-    (synth.Workload("noalloc-big", 1, 2, 16384, 128, 0.1, seed=31), False),
-    (synth.Workload("noalloc-small", 1, 1, 1000, 128, 0.5, seed=32), False),
-    (synth.Workload("noalloc-d64", 2, 2, 2500, 64, 0.3, use_linear=0, seed=33), True),
+    (synth.Workload("noalloc-big", 1, 2, 16384, 128, 0.1, seed=31), "int8"),
+    (synth.Workload("noalloc-small", 1, 1, 1000, 128, 0.5, seed=32), "int8"),
+    (synth.Workload("noalloc-d64", 2, 2, 2500, 64, 0.3, use_linear=0, seed=33), "int8-fine"),
+    (synth.Workload("noalloc-bf16", 1, 2, 3000, 128, 0.2, seed=35), "bf16"),
 ]
 
 
 def test_noalloc_matches_workspace_entry_point():
-    for n, (wl, fine) in enumerate(CALLS):
+    for n, (wl, mode) in enumerate(CALLS):
         q, k, v, w = synth.all_inputs(wl)
         Q, K, V, W = dev(q), dev(k), dev(v), dev(w)
         Wp = W if wl.use_linear else None
         m = sla.SageSLA(wl.B, wl.H, wl.N, wl.d, wl.topk, use_linear=bool(wl.use_linear),
-                        qk_fine=fine)
+                        qk_int8=mode != "bf16", qk_fine=mode == "int8-fine")
         need = m.plan.info.workspace_bytes
         assert need <= sla.NOALLOC_WS_BYTES
         if n > 0:
@@ -51,7 +53,7 @@ def test_noalloc_matches_workspace_entry_point():
         else:
             first_need = need
         say(f"[gpu] noalloc call {n}: {wl.name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} "
-            f"topk={wl.topk} lin={wl.use_linear} fine={fine} workspace={need} bytes")
+            f"topk={wl.topk} lin={wl.use_linear} qk={mode} workspace={need} bytes")
         ref = m.forward(Q, K, V, Wp)
         got = torch.full_like(Q, float("nan"))
         sla.attention_fwd_noalloc(m.plan, Q, K, V, Wp, got)
