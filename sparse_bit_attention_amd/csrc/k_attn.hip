@@ -18,7 +18,9 @@
 // The S^T accumulator puts one query and 16 keys in each lane, so a lane's
 // probabilities are already the B operand of the PV product (the V fragments
 // are stored in the matching key order).  m is a per-row upper bound of the
-// logits (Cauchy-Schwarz on the operands), so no running max is kept; query
+// logits (Cauchy-Schwarz on the operands; bf16: of the logits minus
+// c (q . mu), that constant added to the row's offset, with the key norms
+// taken around the K mean), so no running max is kept; query
 // blocks whose bound is too loose go to a second launch (INT8: online max;
 // bf16: the rows' exact maxima first).  Row sums come from the matrix core
 // (a ones operand, zero at the padding keys of a head's ragged last block).
@@ -41,7 +43,7 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 // probability exp2(logit - m) is at least 2^(-2m): with m <= 48 that is 2^-96,
 // which keeps each probability, the row sum and every P*V product far inside
 // the float32 normal range (2^-126) even when all of a row's kept logits sit
-// near -m.  Rows with a larger bound go to the online-max launch.
+// near -m.  Rows with a larger bound go to the second launch.
 constexpr float BOUND_LIMIT = 48.0f;
 
 template <int D>
