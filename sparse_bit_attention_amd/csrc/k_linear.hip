@@ -248,12 +248,13 @@ __global__ __launch_bounds__(256) void k_kv_prep(const uint16_t *__restrict__ K,
 }
 
 // Projection W [d_out][d_in] into wfrag_off order (A operand, k = d_in).
-__global__ void k_w_swizzle(const uint16_t *__restrict__ W, int D, uint16_t *__restrict__ wsw) {
-  const int KC32 = D / 32;
-  for (int x = threadIdx.x; x < D * D; x += blockDim.x) {
-    const int row = x / D, k = x - row * D;
-    wsw[wfrag_off(row, k, KC32)] = W[x];
-  }
+// one element per thread, D*D/256 workgroups
+__global__ __launch_bounds__(256) void k_w_swizzle(const uint16_t *__restrict__ W, int D,
+                                                   uint16_t *__restrict__ wsw) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= D * D) return;
+  const int row = x / D, k = x - row * D;
+  wsw[wfrag_off(row, k, D / 32)] = W[x];
 }
 
 // H[i][f] = sum_j (1 - M[i][j]) Hb[j][f]: per head a [T x T] by [T x F] GEMM,
@@ -534,7 +535,7 @@ void launch_kv_prep(const Plan &p, const uint16_t *k, const uint16_t *v, const W
 }
 
 void launch_w_swizzle(const Plan &p, const uint16_t *w, const WsPtrs &ws, hipStream_t st) {
-  hipLaunchKernelGGL(k_w_swizzle, dim3(1), dim3(256), 0, st, w, p.d, ws.wsw);
+  hipLaunchKernelGGL(k_w_swizzle, dim3((p.d * p.d + 255) / 256), dim3(256), 0, st, w, p.d, ws.wsw);
 }
 
 void launch_marginal(const Plan &p, const WsPtrs &ws, hipStream_t st) {
