@@ -1009,15 +1009,33 @@ __global__ __launch_bounds__(256, 1) void k_attn(
     v4u pq[4][KC32];
     float den[4];
     const uint16_t *hp = hi + (size_t)qb * F;
+    // Every global load of the branch except the projection's (Q rows, z_i,
+    // H_i fragments) is issued here, before any of them is used, so their
+    // latencies overlap: issued round by round, each waited for before the
+    // next, they left the SIMD idle for most of the epilogue (its only wave).
+    uint4 qv[4][KC32], zv[KC32];
+    v4u hfa[CG][KC32];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int row = i * BLK + 16 * u + l16;
-      const bool ok = row < N;
+      const uint16_t *qr = Q + ((size_t)bh * N + (row < N ? row : 0)) * D;
+#pragma unroll
+      for (int kc = 0; kc < KC32; ++kc) qv[u][kc] = *(const uint4 *)(qr + 32 * kc + 8 * g);
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC32; ++kc) zv[kc] = *(const uint4 *)(hp + D * D + 32 * kc + 8 * g);
+#pragma unroll
+    for (int x = 0; x < CG; ++x)
+#pragma unroll
+      for (int kc = 0; kc < KC32; ++kc)
+        hfa[x][kc] = *(const v4u *)(hp + ((size_t)(x * KC32 + kc) * 64 + lane) * 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       float x[KC32][8];
-      const uint16_t *qr = Q + ((size_t)bh * N + (ok ? row : 0)) * D;
 #pragma unroll
       for (int kc = 0; kc < KC32; ++kc) {
-        uint4 v = *(const uint4 *)(qr + 32 * kc + 8 * g);
+        const uint4 v = qv[u][kc];
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[kc][e] = bf2f((uint16_t)(vv[e >> 1] >> (16 * (e & 1))));
@@ -1043,8 +1061,7 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       float dd = 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC32; ++kc) {
-        uint4 zv = *(const uint4 *)(hp + D * D + 32 * kc + 8 * g);
-        const uint32_t zz[4] = {zv.x, zv.y, zv.z, zv.w};
+        const uint32_t zz[4] = {zv[kc].x, zv[kc].y, zv[kc].z, zv[kc].w};
         uint32_t pk[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -1058,49 +1075,42 @@ __global__ __launch_bounds__(256, 1) void k_attn(
       dd += __shfl_xor(dd, 32, 64);
       den[u] = dd;
     }
-    // O_l^T = H^T phi(Q)^T
-    v4f ol[CG][4];
+    // O_l^T = H^T phi(Q)^T, taken two channel groups at a time and packed at
+    // once into B fragments of O_l^T * (l / den) (k = value channel, kmaj
+    // order), so that O += W (O_l^T l) keeps the sparse sum unnormalised: the
+    // final 1/l then yields O_s + O_l W^T.
+    float rr[4];
 #pragma unroll
-    for (int x = 0; x < CG; ++x) {
-      v4u hf[KC32];
-#pragma unroll
-      for (int kc = 0; kc < KC32; ++kc)
-        hf[kc] = *(const v4u *)(hp + ((size_t)(x * KC32 + kc) * 64 + lane) * 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v4f a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < KC32; ++kc) a = mfma_bf16(hf[kc], pq[u][kc], a);
-        ol[x][u] = a;
-      }
-    }
-    // B fragments of O_l^T * (l / den) (k = value channel, kmaj order), so
-    // that O += W (O_l^T l) keeps the sparse sum unnormalised: the final
-    // 1/l then yields O_s + O_l W^T.
+    for (int u = 0; u < 4; ++u) rr[u] = den[u] > 0.f ? lrow[u] / den[u] : 0.f;
     v4u ob[KC32][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float r = den[u] > 0.f ? lrow[u] / den[u] : 0.f;
+    for (int kc = 0; kc < KC32; ++kc) {
 #pragma unroll
-      for (int kc = 0; kc < KC32; ++kc) {
-        const uint32_t f0 = pack2bf(ol[2 * kc][u][0] * r, ol[2 * kc][u][1] * r);
-        const uint32_t f1 = pack2bf(ol[2 * kc][u][2] * r, ol[2 * kc][u][3] * r);
-        const uint32_t f2 = pack2bf(ol[2 * kc + 1][u][0] * r, ol[2 * kc + 1][u][1] * r);
-        const uint32_t f3 = pack2bf(ol[2 * kc + 1][u][2] * r, ol[2 * kc + 1][u][3] * r);
-        ob[kc][u] = v4u{f0, f1, f2, f3};
+      for (int u = 0; u < 4; ++u) {
+        v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KC32; ++k) {
+          a0 = mfma_bf16(hfa[2 * kc][k], pq[u][k], a0);
+          a1 = mfma_bf16(hfa[2 * kc + 1][k], pq[u][k], a1);
+        }
+        const float r = rr[u];
+        ob[kc][u] = v4u{pack2bf(a0[0] * r, a0[1] * r), pack2bf(a0[2] * r, a0[3] * r),
+                        pack2bf(a1[0] * r, a1[1] * r), pack2bf(a1[2] * r, a1[3] * r)};
       }
     }
+    // The projection's fragments are all requested before the first is used.
+    v4u wf[CG][KC32];
 #pragma unroll
-    for (int y = 0; y < CG; ++y) {
-      v4u wf[KC32];
+    for (int y = 0; y < CG; ++y)
 #pragma unroll
       for (int kc = 0; kc < KC32; ++kc)
-        wf[kc] = *(const v4u *)(wsw + ((size_t)(y * KC32 + kc) * 64 + lane) * 8);
+        wf[y][kc] = *(const v4u *)(wsw + ((size_t)(y * KC32 + kc) * 64 + lane) * 8);
+#pragma unroll
+    for (int y = 0; y < CG; ++y)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int kc = 0; kc < KC32; ++kc) o[y][u] = mfma_bf16(wf[kc], ob[kc][u], o[y][u]);
-    }
+        for (int kc = 0; kc < KC32; ++kc) o[y][u] = mfma_bf16(wf[y][kc], ob[kc][u], o[y][u]);
   }
 
   // store O / l: lane holds query 16u + l16, channels 16a + 4g .. +3.  The
