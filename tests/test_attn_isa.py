@@ -5,7 +5,7 @@ this test compiles csrc/k_attn.hip for gfx950 and checks, on the generated
 code along every control-flow path (loop back-edges included), the wait
 states the CDNA3/CDNA4 matrix cores need around an XDL MFMA of up to 16
 passes, counting one wait state per instruction (the least an issued
-instruction takes):
+instruction takes) and N + 1 for an s_nop N:
 
 * READ_GAP: no instruction other than an MFMA accumulating into exactly the
   same registers reads an asm MFMA's destination sooner (a VALU, memory or
@@ -28,7 +28,7 @@ from sparse_bit_attention_amd import build
 READ_GAP = 24
 WAR_GAP = 16
 VALU_GAP = 2
-SRC = os.path.join(build.CSRC, "k_attn.hip")
+SRCS = ["k_attn.hip"]
 
 
 def vregs(tok):
@@ -97,6 +97,12 @@ def parse(path):
     return kernels
 
 
+def wait_states(text):
+    """Wait states an instruction provides: N + 1 for s_nop N, else 1."""
+    op, ops = operands(text)
+    return int(ops[0], 0) + 1 if op == "s_nop" and ops else 1
+
+
 def successors(ins, labels, j):
     op, ops = operands(ins[j][0])
     if op == "s_endpgm":
@@ -139,7 +145,7 @@ def violations(ins, labels):
             if ins[j][0].startswith("v_") and not ins[j][0].startswith("v_mfma"):
                 if reads_writes(ins[j][0])[1] & srcs:
                     bad.append((ins[j][0], text, -dist, "VALU writes an operand"))
-            back.extend((k, dist + 1) for k in pred[j])
+            back.extend((k, dist + wait_states(ins[j][0])) for k in pred[j])
         # walk every path for READ_GAP instructions; live: the result is still
         # this MFMA's (not yet taken over by an accumulation or overwritten)
         stack = [(j, 1, True) for j in successors(ins, labels, i)]
@@ -169,7 +175,7 @@ def violations(ins, labels):
                     bad.append((text, utext, dist, "overwrites srcC"))
                 if w & dst and not (r & dst):
                     live = False  # the result is dead on this path
-            stack.extend((k, dist + 1, live) for k in successors(ins, labels, j))
+            stack.extend((k, dist + wait_states(utext), live) for k in successors(ins, labels, j))
     return n_asm, bad
 
 
@@ -177,13 +183,16 @@ def violations(ins, labels):
 def isa(tmp_path_factory):
     if not shutil.which(build.HIPCC) and not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("isa") / "k_attn.s")
-    flags = [f for f in build.FLAGS if f not in ("-fPIC",)]
-    cmd = [build.HIPCC, *flags, *build.EXTRA.get("k_attn.hip", []), "--cuda-device-only", "-S", SRC,
-           "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return parse(out)
+    kernels = {}
+    for src in SRCS:
+        out = str(tmp_path_factory.mktemp("isa") / (src + ".s"))
+        flags = [f for f in build.FLAGS if f not in ("-fPIC",)]
+        cmd = [build.HIPCC, *flags, *build.EXTRA.get(src, []), "--cuda-device-only", "-S",
+               os.path.join(build.CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        kernels.update(parse(out))
+    return kernels
 
 
 # the d = 128 pipelined (bound-path) instances, mangled:
@@ -229,6 +238,14 @@ def test_checker_catches_an_early_read():
            ("v_mov_b32_e32 v17, 0", False), ("s_endpgm", False)]
     n, bad = violations(ins, {})
     assert n == 2 and [b[3] for b in bad] == ["overwrites srcC"]
+    # an s_nop 7 provides eight wait states: a read after three of them is far enough
+    ins = [("v_mfma_i32_16x16x64_i8 v[4:7], v[8:11], v[12:15], v[16:19]", True)] + [
+        ("s_nop 7", False)] * 3 + [("v_mov_b32_e32 v0, v5", False), ("s_endpgm", False)]
+    n, bad = violations(ins, {})
+    assert n == 1 and not bad
+    ins = ins[:2] + ins[4:]
+    n, bad = violations(ins, {})
+    assert bad and bad[0][3] == "reads the result"
     # a vector write of an operand right before the MFMA
     ins = [("v_mov_b32_e32 v9, 0", False),
            ("v_mfma_i32_16x16x64_i8 v[4:7], v[8:11], v[12:15], v[16:19]", True),
