@@ -134,9 +134,10 @@ class Workload:
         return [(b, h) for b in range(self.B) for h in range(self.H)]
 
 
-# The five workloads: a tiny case, three Wan-shaped self-attention layers
-# (latent 21 frames x 30 x 52 for 480P, 21 x 45 x 80 for 720P) and a dense
-# INT8 stress case with outlier K channels.
+# The workloads: a tiny case, three Wan-shaped self-attention layers
+# (latent 21 frames x 30 x 52 for 480P, 21 x 45 x 80 for 720P), a dense
+# INT8 stress case with outlier K channels, and the 720P layer's per-GPU share
+# under head sharding.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 2, 1024, 64, 0.25),
     "wan1.3b-480p": Workload("wan1.3b-480p", 1, 12, 21 * 30 * 52, 128, 0.10),
@@ -144,6 +145,10 @@ WORKLOADS = {
     "wan14b-720p": Workload("wan14b-720p", 1, 40, 21 * 45 * 80, 128, 0.10),
     "dense-outlier": Workload("dense-outlier", 2, 12, 21 * 30 * 52, 128, 1.0, use_linear=0,
                               koff_std=4.0, outlier_frac=0.01, outlier_scale=20.0),
+    # One GPU's share of the 720P layer when its 40 heads are split over 8
+    # GPUs: 5 heads.  The generators are keyed by the flat element index, so
+    # these are exactly heads 0..4 of "wan14b-720p".
+    "wan14b-720p-shard8": Workload("wan14b-720p-shard8", 1, 5, 21 * 45 * 80, 128, 0.10),
 }
 
 

@@ -6,6 +6,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 from sparse_bit_attention_amd import synth
@@ -44,6 +45,18 @@ def test_attention_work_at_720p():
     # no linear term when every block is kept
     wl1 = synth.Workload("all", 1, 1, 640, 128, 1.0)
     assert b.attn_work(wl1, 10, 10)[1] == 10 * 10 * 2 * 64 * 64 * 128
+
+
+def test_shard_workload_is_the_first_heads_of_720p():
+    """The per-GPU share under 8-way head sharding is heads 0..4 of the 720P
+    layer itself: same shapes, and the same Q, K, V for its first and last
+    head (the generators are keyed by the flat element index)."""
+    full, shard = synth.WORKLOADS["wan14b-720p"], synth.WORKLOADS["wan14b-720p-shard8"]
+    assert (shard.B, shard.H * 8, shard.N, shard.d, shard.topk) == (full.B, full.H, full.N, full.d, full.topk)
+    for h in (0, shard.H - 1):
+        for a, c in zip(synth.head_inputs(shard, 0, h), synth.head_inputs(full, 0, h)):
+            assert np.array_equal(a, c)
+    assert np.array_equal(synth.proj_weight(shard), synth.proj_weight(full))
 
 
 def test_backward_work_at_720p():

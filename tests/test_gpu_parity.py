@@ -353,6 +353,14 @@ def test_full_size_sampled_parity(name):
         for n, (_, i, j) in enumerate(pairs):
             assert np.array_equal(tiles[n], oracle.qk_int32(prep.q8, prep.k8, i, j))
     assert_close(np.concatenate(G), np.concatenate(R), name)
+    if name == "wan14b-720p":
+        # head sharding: one GPU's share (heads 0..4) alone gives exactly
+        # those heads of the full layer, bit for bit
+        sw = synth.WORKLOADS["wan14b-720p-shard8"]
+        del m, o, dv
+        torch.cuda.empty_cache()
+        _, os_, _, _ = run(sw, inputs=(q[:, :sw.H], k[:, :sw.H], v[:, :sw.H], w))
+        assert np.array_equal(host_u16(os_), out[:, :sw.H])
 
 
 def test_long_sequence_selection():
