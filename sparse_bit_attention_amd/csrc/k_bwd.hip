@@ -66,6 +66,21 @@ __device__ __forceinline__ void tile_load(const uint16_t *src, int nvalid,
   }
 }
 
+// The same rows for the two sparse loops, whose padding rows never reach a
+// product with a nonzero weight (padding queries: normaliser +inf, so P = 0;
+// padding keys: dS = 0): rows >= nvalid read row nvalid - 1 instead of 0, so
+// every load is unconditional.
+template <int D>
+__device__ __forceinline__ void tile_load_clamped(const uint16_t *src, int nvalid,
+                                                  uint4 (&r)[BTile<D>::NPT], int tid) {
+#pragma unroll
+  for (int e = 0; e < BTile<D>::NPT; ++e) {
+    const int x = tid + 256 * e;
+    const int row = x / (D / 8), c8 = (x - row * (D / 8)) * 8;
+    r[e] = *(const uint4 *)(src + (size_t)min(row, nvalid - 1) * D + c8);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void tile_store(const uint4 (&r)[BTile<D>::NPT], uint16_t *lds, int tid) {
 #pragma unroll
@@ -452,8 +467,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
     uint4 rk[NPT], rv[NPT];
     {
       const int j = kl[0];
-      tile_load<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
-      tile_load<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
+      tile_load_clamped<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
+      tile_load_clamped<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
       tile_store_sw<D>(rk, ra, tid);
       tile_store_sw<D>(rv, ra + ST, tid);
     }
@@ -462,8 +477,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
       const int cur = n & 1;
       if (n + 1 < kb) {
         const int j = kl[n + 1];
-        tile_load<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
-        tile_load<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
+        tile_load_clamped<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
+        tile_load_clamped<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
       }
       const uint16_t *sk = ra + 2 * cur * ST, *sv = sk + ST;
       const int nj = min(BLK, N - kl[n] * BLK);  // padding keys get dS = 0
@@ -689,8 +704,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
   float lsn = INFINITY, dn = 0.f;
   auto load_block = [&](int i) {
     const int ni = min(BLK, N - i * BLK);
-    tile_load<D>(Q + (headrow + (size_t)i * BLK) * D, ni, rq, tid);
-    tile_load<D>(dO + (headrow + (size_t)i * BLK) * D, ni, ro, tid);
+    tile_load_clamped<D>(Q + (headrow + (size_t)i * BLK) * D, ni, rq, tid);
+    tile_load_clamped<D>(dO + (headrow + (size_t)i * BLK) * D, ni, ro, tid);
     if (tid < BLK) {
       const size_t qb = (size_t)bh * T + i;
       lsn = tid < ni ? lse[qb * BLK + tid] : INFINITY;  // padding rows: P = 0
