@@ -117,12 +117,17 @@ __device__ __forceinline__ void tile_store_sw(const uint4 (&r)[BTile<D>::NPT], u
   }
 }
 
-// lds_rows on a swizzled tile
+// lds_rows on a swizzled tile.  The two 8-byte reads are volatile so that
+// each lands in its own half of the operand: left to itself the compiler
+// pairs halves of neighbouring fragments into one ds_read2st64_b64 and then
+// spends a register move per dword putting them back together.
 template <int D>
 __device__ __forceinline__ v4u sw_rows(const uint16_t *tile, int r0, int kc, int lane) {
+  typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+  typedef const volatile __attribute__((address_space(3))) u2v lds_u2v;
   const int r = r0 + (lane & 15), k0 = 32 * kc + 4 * (lane >> 4);
-  const uint2 lo = *(const uint2 *)(tile + sw_off<D>(r, k0));
-  const uint2 hi = *(const uint2 *)(tile + sw_off<D>(r, k0 + 16));
+  const u2v lo = *(lds_u2v *)(tile + sw_off<D>(r, k0));
+  const u2v hi = *(lds_u2v *)(tile + sw_off<D>(r, k0 + 16));
   return v4u{lo.x, lo.y, hi.x, hi.y};
 }
 
