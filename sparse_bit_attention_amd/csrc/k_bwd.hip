@@ -92,17 +92,28 @@ __device__ __forceinline__ void tile_store(const uint4 (&r)[BTile<D>::NPT], uint
 }
 
 // Tiles of the two sparse loops: 64 rows of D bf16 without padding, the
-// 4-element (8-byte) units of row r XOR-swizzled by sw_unit(r).  The row
-// reads of an MFMA operand (16 consecutive rows at one unit) and the
-// transposing reads (4 consecutive rows at 4 consecutive units) then fall on
-// distinct banks; with a padded pitch one of the two patterns always
-// conflicts.
-__device__ __forceinline__ int sw_unit(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 4-element (8-byte) units of row r XOR-swizzled by sw_unit<D>(r).  The LDS
+// has 64 four-byte banks and serves an 8-byte read 32 lanes at a time, so
+// each half-wave must touch 32 distinct 8-byte slots modulo 256 bytes:
+//  * row reads of an MFMA operand: lanes l%16 read 16 consecutive rows at
+//    unit u + l/16; with D = 128 the XOR is even and takes 16 distinct
+//    values over any 16 consecutive rows, so the two unit parities of a
+//    half-wave fill all 32 slots;
+//  * transposing reads: a half-wave reads rows 8m .. 8m+7 at units
+//    4x .. 4x+3; bits 2-4 of the XOR are row % 8, distinct over those rows.
+// Even XOR values keep a row's unit pairs (2m, 2m+1) adjacent, so a thread
+// stores its 16 bytes with one instruction.  With D = 64 (16 units, a row
+// of 128 bytes) the XOR has four bits and separates 16 consecutive rows.
+template <int D>
+__device__ __forceinline__ int sw_unit(int r) {
+  if constexpr (D == 128) return ((r & 7) << 2) | ((r >> 2) & 2);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 // element offset of (r, c) for c % 4 == 0
 template <int D>
 __device__ __forceinline__ int sw_off(int r, int c) {
-  return r * D + ((((c >> 2) ^ sw_unit(r))) << 2);
+  return r * D + ((((c >> 2) ^ sw_unit<D>(r))) << 2);
 }
 
 template <int D>
@@ -112,8 +123,12 @@ __device__ __forceinline__ void tile_store_sw(const uint4 (&r)[BTile<D>::NPT], u
   for (int e = 0; e < BTile<D>::NPT; ++e) {
     const int x = tid + 256 * e;
     const int row = x / (D / 8), c8 = (x - row * (D / 8)) * 8;
-    *(uint2 *)(lds + sw_off<D>(row, c8)) = make_uint2(r[e].x, r[e].y);
-    *(uint2 *)(lds + sw_off<D>(row, c8 + 4)) = make_uint2(r[e].z, r[e].w);
+    if constexpr (D == 128) {
+      *(uint4 *)(lds + sw_off<D>(row, c8)) = make_uint4(r[e].x, r[e].y, r[e].z, r[e].w);
+    } else {
+      *(uint2 *)(lds + sw_off<D>(row, c8)) = make_uint2(r[e].x, r[e].y);
+      *(uint2 *)(lds + sw_off<D>(row, c8 + 4)) = make_uint2(r[e].z, r[e].w);
+    }
   }
 }
 
