@@ -96,6 +96,11 @@ def measured_peaks(skip=False):
         "per_instruction_T": {k: v / 1e12 for k, v in r["mfma"].items()},
         "how": "MFMA-only kernels, 8 waves per SIMD, independent accumulator chains, best of 3 "
                "launches of ~25 ms; copy = torch device copy of 1 GiB (read + write bytes)",
+        "issue_cycles_per_slot": peak.issue_table(),
+        "issue_how": "shader-clock cycles (s_memtime) one SIMD takes per instruction slot: per "
+                     "workgroup the span from the first wave's start to the last wave's end over "
+                     "the slots run per SIMD (8 per round, 4000 rounds), 1 or 2 waves per SIMD "
+                     "running the same mix, every compute unit",
     }
 
 

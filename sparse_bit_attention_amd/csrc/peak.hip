@@ -18,6 +18,18 @@
 //     Returns 0, 1 for a bad argument, 2 for a launch error.
 //   long long slapeak_mfma_ops(int kind, int iters, int grid)
 //     integer ops / flops one such launch executes (2 M N K per MFMA).
+//   int slapeak_issue(int kind, int wps, int iters, int grid, long long *cyc,
+//                     int *dig, hipStream_t st)
+//     Issue-rate probe: grid workgroups of 8 waves, of which the first
+//     4 * wps (wps = 1 or 2 waves per SIMD) run iters rounds of one
+//     instruction mix, the rest exit at once.  kind 0: 8 independent
+//     v_fma_f32; 1: 8 independent v_exp_f32; 2: 8 v_mfma_f32_16x16x32_bf16
+//     (8 chains); 3: the same 8 MFMAs, each followed by two independent
+//     v_fma_f32.  cyc: device int64[grid * 8 * 4], per wave the shader
+//     clock (s_memtime) and the 100 MHz real-time clock (s_memrealtime) at
+//     the start and at the end of its rounds (all 0 for waves that exited);
+//     dig: device int32[grid * 8] digests.  Returns 0, 1 for a bad argument,
+//     2 for a launch error.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,7 +108,82 @@ __global__ __launch_bounds__(256) void k_peak(int iters, int *__restrict__ out) 
   if ((tid & 63) == 0) out[blockIdx.x * 4 + (tid >> 6)] = dig;
 }
 
+// Issue-rate probe (see the C ABI note at the top).  The vector instructions
+// are written as inline asm so the compiler neither merges nor reorders
+// them; each result is read again only rounds later.
+template <int KIND>
+__global__ __launch_bounds__(512) void k_issue(int iters, int wps, long long *__restrict__ cyc,
+                                               int *__restrict__ dig) {
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int slot = blockIdx.x * 8 + w;
+  if (w >= 4 * wps) {
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cyc[slot * 4 + e] = 0;
+      dig[slot] = 0;
+    }
+    return;
+  }
+  float a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0.25f + 0.01f * (float)i + 1e-4f * (float)(tid & 63);
+    b[i] = -a[i];
+  }
+  const uint32_t u = 0x3C803C80u + (uint32_t)(tid & 3);
+  const v8bf x = __builtin_bit_cast(v8bf, v4i{(int)u, (int)u, (int)(u ^ 1u), (int)u});
+  v4f c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = v4f{(float)i, 0.f, 0.f, 0.f};
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KIND == 0) {
+        asm volatile("v_fma_f32 %0, %1, %1, %0" : "+v"(b[i]) : "v"(a[i]));
+      } else if constexpr (KIND == 1) {
+        asm volatile("v_exp_f32 %0, %1" : "=v"(b[i]) : "v"(a[i]));
+      } else {
+        c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, x, c[i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KIND == 3) {
+          asm volatile("v_fma_f32 %0, %1, %1, %0" : "+v"(b[i]) : "v"(a[i]));
+          asm volatile("v_fma_f32 %0, %1, %1, %0" : "+v"(a[(i + 4) & 7]) : "v"(b[(i + 2) & 7]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  int d = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    d = d * 3 + __builtin_bit_cast(int, a[i] + b[i]) + __builtin_bit_cast(int, c[i][0] + c[i][3]);
+  if ((tid & 63) == 0) {
+    cyc[slot * 4 + 0] = t0;
+    cyc[slot * 4 + 1] = t1;
+    cyc[slot * 4 + 2] = r0;
+    cyc[slot * 4 + 3] = r1;
+    dig[slot] = d;
+  }
+}
+
 }  // namespace slapeak
+
+extern "C" int slapeak_issue(int kind, int wps, int iters, int grid, long long *cyc, int *dig,
+                             hipStream_t st) {
+  using namespace slapeak;
+  if (kind < 0 || kind > 3 || wps < 1 || wps > 2 || iters < 1 || grid < 1 || !cyc || !dig) return 1;
+  switch (kind) {
+    case 0: k_issue<0><<<grid, 512, 0, st>>>(iters, wps, cyc, dig); break;
+    case 1: k_issue<1><<<grid, 512, 0, st>>>(iters, wps, cyc, dig); break;
+    case 2: k_issue<2><<<grid, 512, 0, st>>>(iters, wps, cyc, dig); break;
+    default: k_issue<3><<<grid, 512, 0, st>>>(iters, wps, cyc, dig); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" long long slapeak_mfma_ops(int kind, int iters, int grid) {
   if (kind < 0 || kind > 3 || iters < 0 || grid < 0) return -1;

@@ -34,6 +34,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_void_p]
         L.slapeak_mfma_ops.restype = ctypes.c_longlong
         L.slapeak_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.slapeak_issue.restype = ctypes.c_int
+        L.slapeak_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -92,6 +95,51 @@ def copy_rate(nbytes: int = 1 << 30, reps: int = 5) -> float:
     e1.record()
     torch.cuda.synchronize()
     return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+
+
+# issue-probe kinds: (name, instructions per slot); a round is 8 slots
+ISSUE_KINDS = {
+    0: ("v_fma_f32", 1),
+    1: ("v_exp_f32", 1),
+    2: ("v_mfma_f32_16x16x32_bf16", 1),
+    3: ("v_mfma_f32_16x16x32_bf16 + 2 v_fma_f32", 3),
+}
+
+
+def issue_cycles(kind: int, wps: int, iters: int = 4000) -> dict:
+    """One launch (after an untimed one) of the issue probe on every compute
+    unit, wps waves per SIMD running the same mix.  Returns the shader-clock
+    cycles per slot (one instruction, or for kind 3 one MFMA and the two FMAs
+    after it) that one SIMD takes: per workgroup, the span from the first
+    wave's start to the last wave's end over the slots its waves ran per
+    SIMD, averaged over the workgroups; and the shader clock in GHz (s_memtime
+    ticks over 100 MHz real-time ticks)."""
+    import torch
+    dev = torch.device("cuda:0")
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    cyc = torch.zeros(grid * 8 * 4, dtype=torch.int64, device=dev)
+    dig = torch.zeros(grid * 8, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    L = lib()
+    for _ in range(2):
+        rc = L.slapeak_issue(kind, wps, iters, grid, ctypes.c_void_p(cyc.data_ptr()),
+                             ctypes.c_void_p(dig.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"slapeak_issue(kind={kind}, wps={wps}) failed with {rc}")
+    torch.cuda.synchronize()
+    c = cyc.view(grid, 8, 4)[:, :4 * wps].double().cpu()
+    span = c[:, :, 1].max(dim=1).values - c[:, :, 0].min(dim=1).values
+    rspan = c[:, :, 3].max(dim=1).values - c[:, :, 2].min(dim=1).values
+    slots_per_simd = 8.0 * iters * wps
+    return {"cycles_per_slot_per_simd": float((span / slots_per_simd).mean()),
+            "clock_GHz": float((span / rspan).mean()) * 0.1}
+
+
+def issue_table() -> dict:
+    """The issue probe's cycles per slot and clock for each kind at one and
+    two waves per SIMD."""
+    return {ISSUE_KINDS[k][0]: {f"{w}_wave_per_simd": issue_cycles(k, w) for w in (1, 2)}
+            for k in ISSUE_KINDS}
 
 
 def measure() -> dict:

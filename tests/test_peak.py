@@ -19,7 +19,7 @@ def built():
 
 def test_exports():
     L = ctypes.CDLL(peak.LIB_PATH)
-    for n in ("slapeak_mfma", "slapeak_mfma_ops"):
+    for n in ("slapeak_mfma", "slapeak_mfma_ops", "slapeak_issue"):
         assert hasattr(L, n)
 
 
@@ -41,6 +41,14 @@ def test_bad_arguments_rejected_before_launch():
     assert L.slapeak_mfma_ops(5, 1, 1) == -1
     with pytest.raises(ValueError):
         peak.ops_per_launch(-1, 1, 1)
+    p = ctypes.c_void_p(16)
+    assert L.slapeak_issue(4, 1, 1, 1, p, p, None) == 1
+    assert L.slapeak_issue(0, 0, 1, 1, p, p, None) == 1
+    assert L.slapeak_issue(0, 3, 1, 1, p, p, None) == 1
+    assert L.slapeak_issue(0, 1, 0, 1, p, p, None) == 1
+    assert L.slapeak_issue(0, 1, 1, 0, p, p, None) == 1
+    assert L.slapeak_issue(0, 1, 1, 1, None, p, None) == 1
+    assert L.slapeak_issue(0, 1, 1, 1, p, None, None) == 1
 
 
 @pytest.mark.gpu
@@ -53,3 +61,19 @@ def test_measured_rates_are_plausible():
     c = peak.copy_rate(1 << 28, reps=3)
     print(f"[peak] device copy {c / 1e9:.0f} GB/s", flush=True)
     assert 1e12 < c < 8.2e12
+
+
+@pytest.mark.gpu
+def test_issue_probe_cycles_are_plausible():
+    # a 16x16x32 bf16 MFMA occupies the matrix core 16 cycles at the
+    # published rate, so no slot holding one can take fewer; a lone vector
+    # instruction takes at least one cycle
+    t = peak.issue_table()
+    for name, per_wps in t.items():
+        for wps, r in per_wps.items():
+            c = r["cycles_per_slot_per_simd"]
+            print(f"[issue] {name} {wps}: {c:.1f} cycles per slot per SIMD at "
+                  f"{r['clock_GHz']:.2f} GHz", flush=True)
+            lo = 15.0 if "mfma" in name else 1.0
+            assert lo <= c < 200.0, (name, wps, c)
+            assert 0.5 < r["clock_GHz"] < 3.0, (name, wps, r)
