@@ -97,10 +97,13 @@ def measured_peaks(skip=False):
         "how": "MFMA-only kernels, 8 waves per SIMD, independent accumulator chains, best of 3 "
                "launches of ~25 ms; copy = torch device copy of 1 GiB (read + write bytes)",
         "issue_cycles_per_slot": peak.issue_table(),
+        "operand_bytes_per_cycle_per_cu": peak.stream_table(),
         "issue_how": "shader-clock cycles (s_memtime) one SIMD takes per instruction slot: per "
                      "workgroup the span from the first wave's start to the last wave's end over "
                      "the slots run per SIMD (8 per round, 4000 rounds), 1 or 2 waves per SIMD "
-                     "running the same mix, every compute unit",
+                     "running the same mix, every compute unit; operand rates: 16-byte reads of "
+                     "L1-resident global memory or of LDS by 4 or 8 waves per CU, bytes per "
+                     "s_memtime cycle",
     }
 
 

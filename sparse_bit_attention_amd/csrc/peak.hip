@@ -30,6 +30,17 @@
 //     the start and at the end of its rounds (all 0 for waves that exited);
 //     dig: device int32[grid * 8] digests.  Returns 0, 1 for a bad argument,
 //     2 for a launch error.
+//   int slapeak_stream(int kind, int waves, int iters, int grid, const void *buf,
+//                      long long *cyc, int *dig, hipStream_t st)
+//     Operand-delivery probe: grid workgroups of 8 waves, of which the first
+//     `waves` (1..8) run iters rounds; in round it each reads 8 KiB (16 bytes
+//     per lane, 8 pieces) alternating between two 8 KiB halves of its
+//     workgroup's 16 KiB.  kind 0: global loads from buf (device, at least
+//     grid * 16 KiB, L1-resident after the first rounds); kind 1: LDS reads
+//     (buf unused, may be null).  cyc: device int64[grid * 8 * 2], per wave
+//     s_memtime at the start and the end of its rounds (0 for idle waves);
+//     dig: device int32[grid * 8].  Returns 0, 1 for a bad argument, 2 for a
+//     launch error.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -170,7 +181,60 @@ __global__ __launch_bounds__(512) void k_issue(int iters, int wps, long long *__
   }
 }
 
+// Operand-delivery probe (see the C ABI note at the top).  The piece index
+// passes through an empty asm every round so the reads cannot be hoisted.
+template <int KIND>
+__global__ __launch_bounds__(512) void k_stream(int iters, int waves, const v4i *__restrict__ buf,
+                                                long long *__restrict__ cyc, int *__restrict__ dig) {
+  __shared__ v4i lds[1024];  // 16 KiB
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int slot = blockIdx.x * 8 + w;
+  if constexpr (KIND == 1) {
+    for (int i = tid; i < 1024; i += 512) lds[i] = v4i{i, i ^ 1, i ^ 2, i ^ 3};
+    __syncthreads();
+  }
+  if (w >= waves) {
+    if (lane == 0) {
+      cyc[slot * 2] = 0;
+      cyc[slot * 2 + 1] = 0;
+      dig[slot] = 0;
+    }
+    return;
+  }
+  const v4i *g = buf + (size_t)blockIdx.x * 1024;
+  v4i acc = {0, 0, 0, 0};
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    int base = (it & 1) * 512;
+    asm volatile("" : "+v"(base));
+    v4i x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = KIND == 0 ? g[base + i * 64 + lane] : lds[base + i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= x[i];
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) {
+    cyc[slot * 2] = t0;
+    cyc[slot * 2 + 1] = t1;
+  }
+  if (lane == 0) dig[slot] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace slapeak
+
+extern "C" int slapeak_stream(int kind, int waves, int iters, int grid, const void *buf,
+                              long long *cyc, int *dig, hipStream_t st) {
+  using namespace slapeak;
+  if (kind < 0 || kind > 1 || waves < 1 || waves > 8 || iters < 1 || grid < 1 || !cyc || !dig ||
+      (kind == 0 && !buf))
+    return 1;
+  if (kind == 0)
+    k_stream<0><<<grid, 512, 0, st>>>(iters, waves, (const v4i *)buf, cyc, dig);
+  else
+    k_stream<1><<<grid, 512, 0, st>>>(iters, waves, (const v4i *)buf, cyc, dig);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int slapeak_issue(int kind, int wps, int iters, int grid, long long *cyc, int *dig,
                              hipStream_t st) {

@@ -34,6 +34,10 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_void_p]
         L.slapeak_mfma_ops.restype = ctypes.c_longlong
         L.slapeak_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.slapeak_stream.restype = ctypes.c_int
+        L.slapeak_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
         L.slapeak_issue.restype = ctypes.c_int
         L.slapeak_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -140,6 +144,39 @@ def issue_table() -> dict:
     two waves per SIMD."""
     return {ISSUE_KINDS[k][0]: {f"{w}_wave_per_simd": issue_cycles(k, w) for w in (1, 2)}
             for k in ISSUE_KINDS}
+
+
+def stream_rate(kind: int, waves: int, iters: int = 2000) -> float:
+    """Bytes per shader cycle one compute unit delivers into registers when
+    `waves` waves read 16-byte pieces back to back: kind 0 from its L1 (a
+    16 KiB block of global memory per workgroup), kind 1 from LDS.  Per
+    workgroup the bytes over the span from the first wave's start to the last
+    wave's end, averaged over one launch on every compute unit (after one
+    untimed launch)."""
+    import torch
+    dev = torch.device("cuda:0")
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.zeros(grid * 16384, dtype=torch.uint8, device=dev)
+    cyc = torch.zeros(grid * 8 * 2, dtype=torch.int64, device=dev)
+    dig = torch.zeros(grid * 8, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    L = lib()
+    for _ in range(2):
+        rc = L.slapeak_stream(kind, waves, iters, grid, ctypes.c_void_p(buf.data_ptr()),
+                              ctypes.c_void_p(cyc.data_ptr()), ctypes.c_void_p(dig.data_ptr()),
+                              ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"slapeak_stream(kind={kind}, waves={waves}) failed with {rc}")
+    torch.cuda.synchronize()
+    c = cyc.view(grid, 8, 2)[:, :waves].double().cpu()
+    span = c[:, :, 1].max(dim=1).values - c[:, :, 0].min(dim=1).values
+    return float((waves * 8192.0 * iters / span).mean())
+
+
+def stream_table() -> dict:
+    """L1 and LDS delivery rates (bytes per cycle per CU) at 4 and 8 waves."""
+    return {name: {f"{w}_waves_per_cu": stream_rate(k, w) for w in (4, 8)}
+            for k, name in ((0, "l1_global_load_dwordx4"), (1, "lds_ds_read_b128"))}
 
 
 def measure() -> dict:

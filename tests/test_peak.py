@@ -19,7 +19,7 @@ def built():
 
 def test_exports():
     L = ctypes.CDLL(peak.LIB_PATH)
-    for n in ("slapeak_mfma", "slapeak_mfma_ops", "slapeak_issue"):
+    for n in ("slapeak_mfma", "slapeak_mfma_ops", "slapeak_issue", "slapeak_stream"):
         assert hasattr(L, n)
 
 
@@ -49,6 +49,14 @@ def test_bad_arguments_rejected_before_launch():
     assert L.slapeak_issue(0, 1, 1, 0, p, p, None) == 1
     assert L.slapeak_issue(0, 1, 1, 1, None, p, None) == 1
     assert L.slapeak_issue(0, 1, 1, 1, p, None, None) == 1
+    assert L.slapeak_stream(2, 4, 1, 1, p, p, p, None) == 1
+    assert L.slapeak_stream(0, 0, 1, 1, p, p, p, None) == 1
+    assert L.slapeak_stream(0, 9, 1, 1, p, p, p, None) == 1
+    assert L.slapeak_stream(0, 4, 0, 1, p, p, p, None) == 1
+    assert L.slapeak_stream(0, 4, 1, 0, p, p, p, None) == 1
+    assert L.slapeak_stream(0, 4, 1, 1, None, p, p, None) == 1
+    assert L.slapeak_stream(1, 4, 1, 1, None, None, p, None) == 1
+    assert L.slapeak_stream(1, 4, 1, 1, None, p, None, None) == 1
 
 
 @pytest.mark.gpu
@@ -77,3 +85,14 @@ def test_issue_probe_cycles_are_plausible():
             lo = 15.0 if "mfma" in name else 1.0
             assert lo <= c < 200.0, (name, wps, c)
             assert 0.5 < r["clock_GHz"] < 3.0, (name, wps, r)
+
+
+@pytest.mark.gpu
+def test_operand_rates_are_plausible():
+    # 16-byte reads: at least a few bytes per cycle, and no more than 64
+    # lanes x 16 bytes per cycle from either source
+    t = peak.stream_table()
+    for name, per_w in t.items():
+        for w, r in per_w.items():
+            print(f"[stream] {name} {w}: {r:.1f} bytes per cycle per CU", flush=True)
+            assert 4.0 < r < 1024.0, (name, w, r)
