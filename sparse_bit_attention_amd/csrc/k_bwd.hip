@@ -132,6 +132,36 @@ __device__ __forceinline__ void tile_store_sw(const uint4 (&r)[BTile<D>::NPT], u
   }
 }
 
+// Swizzled 64-row tile (D = 128) straight from global memory into LDS by the
+// load-to-LDS path: an instruction writes lane l's 16 bytes at byte 16 l of
+// a 1 KiB piece (four rows).  sw_unit is even at D = 128, so a 16-byte
+// source piece stays whole under the swizzle, and lane l fetches the piece
+// that tile_store_sw would put at its place.  Rows past nvalid read row
+// nvalid - 1.  Wave w fills rows 16 w .. 16 w + 15 (four instructions).
+__device__ __forceinline__ void bwd_dma16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void bwd_dma4(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ __forceinline__ void tile_dma_sw128(const uint16_t *src, int nvalid, uint16_t *lds,
+                                               int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 16 * w + 4 * e + (lane >> 4), p = lane & 15;
+    const int k = p ^ (sw_unit<128>(r) >> 1);
+    bwd_dma16(src + (size_t)min(r, nvalid - 1) * 128 + 8 * k,
+              __builtin_amdgcn_readfirstlane(base + (uint32_t)((16 * w + 4 * e) * 256)));
+  }
+}
+
 // lds_rows on a swizzled tile.  The two 8-byte reads are volatile so that
 // each lands in its own half of the operand: left to itself the compiler
 // pairs halves of neighbouring fragments into one ds_read2st64_b64 and then
@@ -480,42 +510,83 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
       qf[kc] = v4u{a.x, a.y, b.x, b.y};
       of[kc] = v4u{c.x, c.y, d.x, d.y};
     }
-    const float l2 = q < ni ? lse[(size_t)qb * BLK + q] : INFINITY;  // padding rows: P = 0
+    float l2 = q < ni ? lse[(size_t)qb * BLK + q] : INFINITY;  // padding rows: P = 0
     const float dlt = sdelta[q];
+    // Complete these loads here: left pending, the compiler's wait before
+    // their first use inside the loop also waits for the tile copies the loop
+    // issues for the next kept block.
+#pragma unroll
+    for (int kc = 0; kc < KC32; ++kc) asm volatile("" : "+v"(qf[kc]), "+v"(of[kc]));
+    asm volatile("" : "+v"(l2));
     const int32_t *kl = kept + (size_t)qb * kb;
     const uint16_t *Kh = K + (size_t)bh * N * D, *Vh = V + (size_t)bh * N * D;
-    uint4 rk[NPT], rv[NPT];
-    {
-      const int j = kl[0];
-      tile_load_clamped<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
-      tile_load_clamped<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
-      tile_store_sw<D>(rk, ra, tid);
-      tile_store_sw<D>(rv, ra + ST, tid);
-    }
+    // D = 128: the K and V tiles go straight into LDS buffer b by the
+    // load-to-LDS path (no staging registers); D = 64 stages them in registers.
+    constexpr bool DMA = D == 128;
+    uint4 rk[DMA ? 1 : NPT], rv[DMA ? 1 : NPT];
+    auto load_kv = [&](int j, int b) {
+      const int nj = min(BLK, N - j * BLK);
+      if constexpr (DMA) {
+        tile_dma_sw128(Kh + (size_t)j * BLK * D, nj, ra + 2 * b * ST, tid);
+        tile_dma_sw128(Vh + (size_t)j * BLK * D, nj, ra + (2 * b + 1) * ST, tid);
+      } else {
+        tile_load_clamped<D>(Kh + (size_t)j * BLK * D, nj, rk, tid);
+        tile_load_clamped<D>(Vh + (size_t)j * BLK * D, nj, rv, tid);
+      }
+    };
+    auto store_kv = [&](int b) {
+      if constexpr (DMA) {
+        // the wave's copies have landed; the barrier after this makes all
+        // four waves' copies visible
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        tile_store_sw<D>(rk, ra + 2 * b * ST, tid);
+        tile_store_sw<D>(rv, ra + (2 * b + 1) * ST, tid);
+      }
+    };
+    load_kv(kl[0], 0);
+    store_kv(0);
     __syncthreads();
     for (int n = 0; n < kb; ++n) {
       const int cur = n & 1;
-      if (n + 1 < kb) {
-        const int j = kl[n + 1];
-        tile_load_clamped<D>(Kh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rk, tid);
-        tile_load_clamped<D>(Vh + (size_t)j * BLK * D, min(BLK, N - j * BLK), rv, tid);
-      }
+      if (n + 1 < kb) load_kv(kl[n + 1], cur ^ 1);
       const uint16_t *sk = ra + 2 * cur * ST, *sv = sk + ST;
       const int nj = min(BLK, N - kl[n] * BLK);  // padding keys get dS = 0
       v4f s[4], dp[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = dp[t] = v4f{0.f, 0.f, 0.f, 0.f};
-      // raised wave priority around each block of products, so the other
-      // workgroup's wave on this SIMD does its vector and LDS work meanwhile
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kc = 0; kc < KC32; ++kc)
+      // The fragments of channel chunk kc + 1 (K rows for S, V rows for dP,
+      // four key tiles each) are read before chunk kc's products, so each
+      // read has a whole chunk of products to land.  Raised wave priority
+      // around each block of products, so the other workgroup's wave on this
+      // SIMD does its vector and LDS work meanwhile.
+      v4u fk[2][4], fv[2][4];
+      auto frags = [&](int kc, v4u (&a)[4], v4u (&b)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          s[t] = mfma_bf16(sw_rows<D>(sk, 16 * t, kc, lane), qf[kc], s[t]);
-          dp[t] = mfma_bf16(sw_rows<D>(sv, 16 * t, kc, lane), of[kc], dp[t]);
+          a[t] = sw_rows<D>(sk, 16 * t, kc, lane);
+          b[t] = sw_rows<D>(sv, 16 * t, kc, lane);
         }
+      };
+      frags(0, fk[0], fv[0]);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kc = 0; kc < KC32; ++kc) {
+        if (kc + 1 < KC32) frags(kc + 1, fk[(kc + 1) & 1], fv[(kc + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          s[t] = mfma_bf16(fk[kc & 1][t], qf[kc], s[t]);
+          dp[t] = mfma_bf16(fv[kc & 1][t], of[kc], dp[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_s_setprio(0);
+      // the dQ products' first K fragments, read while dS is formed
+      v4u fq[2][CG];
+#pragma unroll
+      for (int x = 0; x < CG; ++x) fq[0][x] = sw_frag<D>(sk, 0, 16 * x, lane);
+      __builtin_amdgcn_sched_barrier(0);
       // dS^T = P^T (dP^T - D) in the key order of lds_frag (kmaj)
       v4u dsb[2];
 #pragma unroll
@@ -537,16 +608,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(
         }
         dsb[kc2] = v4u{pk[0], pk[1], pk[2], pk[3]};
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < CG; ++x) fq[1][x] = sw_frag<D>(sk, 1, 16 * x, lane);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
-        for (int x = 0; x < CG; ++x) adq[x] = mfma_bf16(sw_frag<D>(sk, kc2, 16 * x, lane), dsb[kc2], adq[x]);
+        for (int x = 0; x < CG; ++x) adq[x] = mfma_bf16(fq[kc2][x], dsb[kc2], adq[x]);
       __builtin_amdgcn_s_setprio(0);
-      if (n + 1 < kb) {
-        tile_store_sw<D>(rk, ra + 2 * (cur ^ 1) * ST, tid);
-        tile_store_sw<D>(rv, ra + (2 * (cur ^ 1) + 1) * ST, tid);
-      }
+      if (n + 1 < kb) store_kv(cur ^ 1);
       __syncthreads();
     }
   }
@@ -720,49 +792,91 @@ __global__ __launch_bounds__(256, 2) void k_bwd_kv(
   };
   const size_t headrow = (size_t)bh * N;
   // buffer b: Q at ra + 2 b ST, dO at ra + (2 b + 1) ST
-  uint4 rq[NPT], ro[NPT];
+  // D = 128: the Q and dO tiles go straight into LDS buffer b by the
+  // load-to-LDS path (no staging registers); D = 64 stages them in registers.
+  constexpr bool DMA = D == 128;
+  uint4 rq[DMA ? 1 : NPT], ro[DMA ? 1 : NPT];
   float lsn = INFINITY, dn = 0.f;
-  auto load_block = [&](int i) {
+  int nin = BLK;  // valid rows of the block being loaded
+  auto load_block = [&](int i, int b) {
     const int ni = min(BLK, N - i * BLK);
-    tile_load_clamped<D>(Q + (headrow + (size_t)i * BLK) * D, ni, rq, tid);
-    tile_load_clamped<D>(dO + (headrow + (size_t)i * BLK) * D, ni, ro, tid);
-    if (tid < BLK) {
-      const size_t qb = (size_t)bh * T + i;
-      lsn = tid < ni ? lse[qb * BLK + tid] : INFINITY;  // padding rows: P = 0
-      dn = tid < ni ? delta[qb * BLK + tid] : 0.f;
+    nin = ni;
+    const size_t qb = (size_t)bh * T + i;
+    if constexpr (DMA) {
+      // wave 0 also copies the row statistics (rows past ni read row ni - 1
+      // and are patched in store_block)
+      if (w == 0) {
+        const int r = min(lane, ni - 1);
+        bwd_dma4(lse + qb * BLK + r, __builtin_amdgcn_readfirstlane(lds_addr(&sl[b][0])));
+        bwd_dma4(delta + qb * BLK + r, __builtin_amdgcn_readfirstlane(lds_addr(&sd[b][0])));
+      }
+      tile_dma_sw128(Q + (headrow + (size_t)i * BLK) * D, ni, ra + 2 * b * ST, tid);
+      tile_dma_sw128(dO + (headrow + (size_t)i * BLK) * D, ni, ra + (2 * b + 1) * ST, tid);
+    } else {
+      if (tid < BLK) {
+        lsn = tid < ni ? lse[qb * BLK + tid] : INFINITY;  // padding rows: P = 0
+        dn = tid < ni ? delta[qb * BLK + tid] : 0.f;
+      }
+      tile_load_clamped<D>(Q + (headrow + (size_t)i * BLK) * D, ni, rq, tid);
+      tile_load_clamped<D>(dO + (headrow + (size_t)i * BLK) * D, ni, ro, tid);
     }
   };
   auto store_block = [&](int b) {
-    tile_store_sw<D>(rq, ra + 2 * b * ST, tid);
-    tile_store_sw<D>(ro, ra + (2 * b + 1) * ST, tid);
-    if (tid < BLK) {
-      sl[b][tid] = lsn;
-      sd[b][tid] = dn;
+    if constexpr (DMA) {
+      // the wave's copies have landed (the barrier after this makes all four
+      // waves' copies visible); padding rows: P = 0
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (w == 0 && lane >= nin) {
+        sl[b][lane] = INFINITY;
+        sd[b][lane] = 0.f;
+      }
+    } else {
+      tile_store_sw<D>(rq, ra + 2 * b * ST, tid);
+      tile_store_sw<D>(ro, ra + (2 * b + 1) * ST, tid);
+      if (tid < BLK) {
+        sl[b][tid] = lsn;
+        sd[b][tid] = dn;
+      }
     }
   };
   int inext = next_i();
   if (inext >= 0) {
-    load_block(inext);
+    load_block(inext, 0);
     store_block(0);
   }
   __syncthreads();
   int buf = 0;
   while (inext >= 0) {
     inext = next_i();
-    if (inext >= 0) load_block(inext);
+    if (inext >= 0) load_block(inext, buf ^ 1);
     const uint16_t *sq = ra + 2 * buf * ST, *so = sq + ST;
     // S and dP: query rows 16t + 4g + r, key column s
     v4f sa[4], dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) sa[t] = dp[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kc = 0; kc < KC32; ++kc)
+    // the Q and dO fragments of channel chunk kc + 1 are read before chunk
+    // kc's products, so each read has a whole chunk of products to land
+    v4u fq[2][4], fo[2][4];
+    auto frags = [&](int kc, v4u (&a)[4], v4u (&b)[4]) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        sa[t] = mfma_bf16(sw_rows<D>(sq, 16 * t, kc, lane), kf[kc], sa[t]);
-        dp[t] = mfma_bf16(sw_rows<D>(so, 16 * t, kc, lane), vf[kc], dp[t]);
+        a[t] = sw_rows<D>(sq, 16 * t, kc, lane);
+        b[t] = sw_rows<D>(so, 16 * t, kc, lane);
       }
+    };
+    frags(0, fq[0], fo[0]);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kc = 0; kc < KC32; ++kc) {
+      if (kc + 1 < KC32) frags(kc + 1, fq[(kc + 1) & 1], fo[(kc + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sa[t] = mfma_bf16(fq[kc & 1][t], kf[kc], sa[t]);
+        dp[t] = mfma_bf16(fo[kc & 1][t], vf[kc], dp[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_s_setprio(0);
     // P and dS as B fragments in the query order of lds_frag
     v4u pb[2], dsb[2];

@@ -85,3 +85,28 @@ def test_d64_row_reads_are_conflict_free():
             for h in range(2):
                 a = [_slot(f, 16, 16 * t + (l & 15), 8 * kc + (l >> 4) + 4 * h) for l in range(64)]
                 assert _worst(a, 16, 16) == 1
+
+
+def test_d128_load_to_lds_copy_matches_the_swizzled_store():
+    # tile_dma_sw128: wave w, instruction e, lane l writes the 16 bytes at
+    # byte 16 l of the 1 KiB piece at rows 16w + 4e .. +3 (LDS row r = 16w +
+    # 4e + l/16, 16-byte chunk p = l % 16) and fetches source chunk
+    # k = p ^ (sw_unit(r) >> 1) of row r.  tile_store_sw puts source unit u
+    # (8 bytes) of row r at unit u ^ sw_unit(r).  Every destination unit must
+    # receive exactly the source unit the swizzled store would put there.
+    f = F128
+    written = {}
+    for w in range(4):
+        for e in range(4):
+            for lane in range(64):
+                r, p = 16 * w + 4 * e + lane // 16, lane % 16
+                assert f(r) % 2 == 0  # a 16-byte piece stays whole under the XOR
+                k = p ^ (f(r) >> 1)
+                for h in range(2):  # the two 8-byte units of the piece
+                    dst = (r, 2 * p + h)
+                    assert dst not in written
+                    written[dst] = (r, 2 * k + h)
+    assert len(written) == 64 * 32
+    for r in range(64):
+        for u in range(32):
+            assert written[(r, u ^ f(r))] == (r, u)
